@@ -23,6 +23,7 @@
  * Parity pins: every function here is checked by tests/test_oracle_*.py against
  * closed forms, invariants, brute force or library routines (see each function).
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -151,8 +152,10 @@ long orc_k_mean(const uint16_t* k, const int64_t* str, int B, int H, int N, int 
 /* H3 Performance Roadmap, "Measured GB10 Baseline" (Q/K INT8 quantization row) and
  * "Phase 4" item 2 (per-warp INT8 Q/K quantization).  Reading: symmetric INT8 with one
  * fp32 scale per block of 64 consecutive rows of one (b, h); a = max |x| over the
- * block's valid rows; s = fl32(a / 127); code = clamp(rne(fl32(x * fl32(127 / a))));
- * a = 0 gives s = 0 and zero codes; rows N..N_pad-1 are zero codes.
+ * block's valid rows; s = fl32(a / 127); r = min(fl32(127 / a), FLT_MAX);
+ * code = clamp(rne(fl32(x * r))); a = 0 gives s = 0 and zero codes; rows N..N_pad-1
+ * are zero codes.  (The clamp of r only acts when a < 127 / FLT_MAX, where the
+ * reciprocal would overflow; the pages are silent on it.)
  * With mean != NULL the value quantized is x' = fl32(x - mean[b,h,c]) (smoothing).
  * x: bf16 [B, N, H, D] strided; codes: int8 [B, H, N_pad, D]; scales: [B, H, N_pad/64]. */
 void orc_quant_i8_blocks(const uint16_t* x, const int64_t* str, const float* mean, int B, int H, int N, int D,
@@ -177,7 +180,7 @@ void orc_quant_i8_blocks(const uint16_t* x, const int64_t* str, const float* mea
         float s = 0.0f, rcp = 0.0f;
         if (a > 0.0f) {
           s = a / 127.0f;
-          rcp = 127.0f / a;
+          rcp = fminf(127.0f / a, FLT_MAX);
         }
         scales[((int64_t)b * H + h) * nblk + blk] = s;
         int8_t* out = codes + (((int64_t)b * H + h) * npad + r0) * D;
@@ -194,7 +197,8 @@ void orc_quant_i8_blocks(const uint16_t* x, const int64_t* str, const float* mea
 /* H3 Performance Roadmap, "Measured GB10 Baseline" (V FP8 quantization row: a combined
  * V transpose and FP8 quantization) and "Phase 4" item 2 (FP8 V policy).  Reading: one
  * fp32 scale per (b, h, channel) over all valid tokens: a = max |v|; s = fl32(a / 448);
- * code = E4M3(fl32(v * fl32(448 / a))); a = 0 gives s = 0 and 0x00 codes.  Output is
+ * r = min(fl32(448 / a), FLT_MAX); code = E4M3(fl32(v * r)); a = 0 gives s = 0 and 0x00
+ * codes.  (As for INT8, the clamp of r only acts when the reciprocal would overflow.)  Output is
  * channel-major (transposed): v8t [B, H, D, N_pad] with zero codes for n >= N.
  * vf: fp32 values [B, H, N, D] already gathered (bf16 inputs or dequantized cache). */
 static void quant_v_f32(const float* vf, int B, int H, int N, int D, uint8_t* v8t, float* vscale) {
@@ -211,7 +215,7 @@ static void quant_v_f32(const float* vf, int B, int H, int N, int D, uint8_t* v8
         float s = 0.0f, rcp = 0.0f;
         if (a > 0.0f) {
           s = a / 448.0f;
-          rcp = 448.0f / a;
+          rcp = fminf(448.0f / a, FLT_MAX);
         }
         vscale[((int64_t)b * H + h) * D + c] = s;
         uint8_t* out = v8t + (((int64_t)b * H + h) * D + c) * (int64_t)npad;

@@ -175,3 +175,20 @@ def test_requant_v_cache(orc):
         assert np.array_equal(v8t[h][:, :Nk].T, orc.e4m3_encode(y))
         assert not v8t[h][:, Nk:].any()
         assert np.all(np.abs(dec[v8t[h][:, :Nk]]).max(axis=1) == 448.0)
+
+
+def test_reciprocal_overflow_clamped(orc):
+    """A block whose absmax is below 127/FLT_MAX: the reciprocal saturates at FLT_MAX
+    instead of overflowing, so codes stay finite (rne(x * FLT_MAX)) and no NaN appears."""
+    fmax = np.float32(np.finfo(np.float32).max)
+    tiny = np.float32(2.0 ** -127)  # a bf16-representable subnormal
+    x = np.zeros((1, 64, 1, 64), np.float32)
+    x[0, :, 0, 0] = tiny
+    x[0, :, 0, 1] = -tiny / 2
+    codes, scales = orc.quant_i8_blocks(W.bf16_bits(x))
+    assert scales[0, 0, 0] == np.float32(tiny / np.float32(127.0))
+    assert np.all(codes[0, 0, :, 0] == np.int8(np.rint(np.float32(tiny * fmax))))
+    assert np.all(codes[0, 0, :, 1] == np.int8(np.rint(np.float32(-tiny / 2 * fmax))))
+    v8t, vs = orc.quant_v(W.bf16_bits(x))
+    assert v8t[0, 0, 0, 0] == orc.e4m3_encode(np.float32([tiny * fmax]))[0]
+    assert v8t[0, 0, 2, 0] == 0x00
