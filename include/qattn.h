@@ -1,0 +1,123 @@
+/*
+ * qattn.h -- C ABI of the quantized attention forward for MI355X (gfx950).
+ *
+ * The method: K smoothing, INT8 Q/K with per-block scales, FP8 e4m3 V with per-channel
+ * scales, INT8 Q.K^T with INT32 accumulation, a tile-ordered online softmax whose P is
+ * converted to FP8, and FP8 P.V with a fused V-scale epilogue ("H3 Performance Roadmap",
+ * sections "Measured GB10 Baseline" and "Phase 4: Dense Sage-Compatible Attention";
+ * "Sage2 SM89 Temporal Pair Experiment", section "Candidate").  Prefill over an INT8 KV
+ * cache with per-token scales follows Strata #2092 (description).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  Nothing is allocated
+ *     or freed by the library.  Shape and stride arrays are HOST pointers.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream) and returns before the GPU work completes.
+ *   - Arguments are validated before any HIP call; on failure the call returns a negative
+ *     qattn_status and launches nothing.  QATTN_EHIP reports a failed launch.
+ *   - Strides are in elements; the innermost (D) stride is always 1.
+ *   - D (head dimension) must be 64 or 128 (QATTN_EUNSUPPORTED otherwise).
+ *   - bf16 inputs: base 16-byte aligned, strides multiples of 8 elements.
+ *     Code buffers (q8, k8, v8t) and the workspace: 256-byte aligned.
+ *     Scale buffers: 4-byte aligned.  Outputs: base and strides aligned to 4 elements.
+ *   - N_pad = ceil(N / 64) * 64.  Code layouts are zero-padded to N_pad rows/columns.
+ *   - Results are bitwise deterministic run to run (no atomics).
+ *   - NaN/Inf inputs are outside the contract (their codes are unspecified).
+ *   - Calls on different streams that share output buffers race; the library holds no
+ *     global mutable state, so calls are otherwise thread-safe.
+ */
+#ifndef QATTN_H
+#define QATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QATTN_OK = 0,
+  QATTN_EINVAL = -1,        /* null pointer, bad size, misalignment, bad stride, pos0 out of range */
+  QATTN_EUNSUPPORTED = -2,  /* D not in {64, 128} */
+  QATTN_EWORKSPACE = -3,    /* workspace smaller than qattn_fwd_i8kv_workspace_bytes() */
+  QATTN_EHIP = -4           /* a kernel launch failed */
+} qattn_status;
+
+typedef enum { QATTN_OUT_BF16 = 0, QATTN_OUT_F32 = 1 } qattn_out_dtype;
+
+/* Step 1 -- K smoothing and INT8 Q/K quantization ("H3 Performance Roadmap", "Measured
+ * GB10 Baseline": K smoothing and Q/K INT8 quantization rows; "Phase 4" items 2-3).
+ *   q: bf16 [B, Nq, H, D] view with element strides q_str = {sb, sn, sh};
+ *   k: bf16 [B, Nk, H, D] view with strides k_str.
+ *   k_mean  f32 [B, H, D]: mu = fl32(fp64 sum over the Nk tokens / Nk);
+ *   q8      int8 [B, H, Nq_pad, D], q_scale f32 [B, H, Nq_pad/64];
+ *   k8      int8 [B, H, Nk_pad, D] of fl32(K - mu), k_scale f32 [B, H, Nk_pad/64].
+ * Per (b, h) block of 64 rows: a = max|x|, scale = fl32(a/127), code =
+ * clamp(rne(fl32(x * min(fl32(127/a), FLT_MAX))), -127, 127); a = 0 gives scale 0 and
+ * zero codes; padding rows are zero.  k8 doubles as scratch for the fp64 partial sums
+ * during the call (its final contents are the codes). */
+int qattn_quant_qk(const void* q, const int64_t q_str[3], const void* k, const int64_t k_str[3], int B, int H,
+                   int Nq, int Nk, int D, int8_t* q8, float* q_scale, int8_t* k8, float* k_scale, float* k_mean,
+                   void* stream);
+
+/* Step 2 -- V FP8 quantization with transpose ("H3 Performance Roadmap", "Measured GB10
+ * Baseline": V transpose/FP8 quantization row; "Phase 4" item 2).
+ *   v: bf16 [B, Nk, H, D] view with strides v_str.
+ *   v8t     OCP e4m3fn bytes, channel-major [B, H, D, Nk_pad] (tokens >= Nk are 0x00);
+ *   v_scale f32 [B, H, D].
+ * Per (b, h, channel): a = max|v| over the Nk tokens, scale = fl32(a/448), code =
+ * E4M3(fl32(v * min(fl32(448/a), FLT_MAX))) rounded to nearest even, saturated at 448,
+ * sign kept; a = 0 gives scale 0 and 0x00 codes.  v8t and v_scale are used as scratch
+ * during the call. */
+int qattn_quant_v(const void* v, const int64_t v_str[3], int B, int H, int Nk, int D, uint8_t* v8t,
+                  float* v_scale, void* stream);
+
+/* Steps 3-5 -- fused INT8 QK, online softmax with FP8 P, FP8 PV and epilogue ("Sage2 SM89
+ * Temporal Pair Experiment", "Candidate": per 64-key tile QK -> update m, d, O ->
+ * accumulate d -> P to 8 bit -> PV), on the outputs of steps 1-2 (same layouts).
+ *   scale_log2: softmax scale times log2(e); <= 0 selects fl32(fl32(1/sqrt(D)) * log2e).
+ *   causal: key j visible to query i iff j <= i + (Nk - Nq) (bottom-right aligned); a
+ *           query with no visible key outputs zeros.
+ *   out: [B, Nq, H, D] view with strides out_str, dtype out_dtype (token-major NHD).
+ * Output = fl32(O * s_v / d') with fp32 accumulation; bf16 output is its RNE rounding. */
+int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale, const uint8_t* v8t,
+              const float* v_scale, int B, int H, int Nq, int Nk, int D, float scale_log2, int causal, void* out,
+              const int64_t out_str[3], int out_dtype, void* stream);
+
+/* Prefill over an INT8 KV cache with per-token scales (Strata #2092, description and
+ * the "qsa_prompt_attn_parity (int8 KV)" table).
+ *   q: bf16 [Nq, H, D] view with strides q_str = {sn, sh}; query i sits at absolute
+ *      position pos0 + i and sees keys 0 .. pos0 + i (0 <= pos0, pos0 + Nq <= Nk).
+ *   k_cache, v_cache: int8 [H, Nk, D] contiguous; k_tok_scale, v_tok_scale: f32 [H, Nk]
+ *      (one scale per head and token: value = code * scale).
+ *   workspace: >= qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D) bytes, 256-byte aligned;
+ *      receives the per-channel e4m3 requantization of V (fl32(code * scale) quantized
+ *      as in step 2 over all Nk tokens) and the INT8 blocks of q (as in step 1, no
+ *      smoothing).
+ *   out: [Nq, H, D] view with strides out_str = {sn, sh}.
+ * K codes are used as stored, with c_j = fl32(fl32(s_q * s_k[j]) * scale_log2). */
+int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache, const float* k_tok_scale,
+                   const int8_t* v_cache, const float* v_tok_scale, int H, int Nq, int Nk, int D, int pos0,
+                   float scale_log2, void* workspace, size_t workspace_bytes, void* out, const int64_t out_str[2],
+                   int out_dtype, void* stream);
+
+/* Workspace size for qattn_fwd_i8kv: H*D*Nk_pad (e4m3 V) + H*D*4 (V scales) +
+ * H*Nq_pad*D (q codes) + H*Nq_pad/64*4 (q scales), each section rounded up to 256 bytes.
+ * Returns 0 for invalid sizes. */
+size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D);
+
+/* Self-test hook: codes[i] = E4M3(exp2(fl32(u[i] - 192))) computed by the fused kernel's
+ * own device function (the FP8 P code the softmax produces for the grid argument u).
+ * u: f32 [n], codes: u8 [n], device pointers.  Used to check the exponential against the
+ * correctly rounded one over the whole argument grid. */
+int qattn_p8_codes(const float* u, uint8_t* codes, int64_t n, void* stream);
+
+/* Static description of a status code. */
+const char* qattn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QATTN_H */

@@ -128,21 +128,26 @@ static int8_t i8_code(float x, float r) {
  * mean: fp32 [B, H, D]. */
 long orc_k_mean(const uint16_t* k, const int64_t* str, int B, int H, int N, int D, float* mean) {
   long inexact = 0;
+  double* s = (double*)malloc(sizeof(double) * D);
   for (int b = 0; b < B; ++b)
-    for (int h = 0; h < H; ++h)
-      for (int c = 0; c < D; ++c) {
-        double s = 0.0;
-        for (int n = 0; n < N; ++n) {
-          double x = (double)orc_bf16_to_f32(k[b * str[0] + (int64_t)n * str[1] + h * str[2] + c]);
-          double t = s + x;
+    for (int h = 0; h < H; ++h) {
+      for (int c = 0; c < D; ++c) s[c] = 0.0;
+      /* each channel's sum runs over n = 0, 1, ..., N-1 in order */
+      for (int n = 0; n < N; ++n) {
+        const uint16_t* row = k + b * str[0] + (int64_t)n * str[1] + h * str[2];
+        for (int c = 0; c < D; ++c) {
+          double x = (double)orc_bf16_to_f32(row[c]);
+          double t = s[c] + x;
           /* TwoSum error term */
-          double bp = t - s;
-          double err = (s - (t - bp)) + (x - bp);
+          double bp = t - s[c];
+          double err = (s[c] - (t - bp)) + (x - bp);
           if (err != 0.0) inexact++;
-          s = t;
+          s[c] = t;
         }
-        mean[((int64_t)b * H + h) * D + c] = (float)(s / (double)N);
       }
+      for (int c = 0; c < D; ++c) mean[((int64_t)b * H + h) * D + c] = (float)(s[c] / (double)N);
+    }
+  free(s);
   return inexact;
 }
 
@@ -203,26 +208,34 @@ void orc_quant_i8_blocks(const uint16_t* x, const int64_t* str, const float* mea
  * vf: fp32 values [B, H, N, D] already gathered (bf16 inputs or dequantized cache). */
 static void quant_v_f32(const float* vf, int B, int H, int N, int D, uint8_t* v8t, float* vscale) {
   int npad = (N + ORC_TILE - 1) / ORC_TILE * ORC_TILE;
+  float* a = (float*)malloc(sizeof(float) * D);
+  float* rcp = (float*)malloc(sizeof(float) * D);
   for (int b = 0; b < B; ++b)
     for (int h = 0; h < H; ++h) {
       const float* src = vf + ((int64_t)b * H + h) * (int64_t)N * D;
-      for (int c = 0; c < D; ++c) {
-        float a = 0.0f;
-        for (int n = 0; n < N; ++n) {
+      uint8_t* out = v8t + ((int64_t)b * H + h) * D * (int64_t)npad;
+      for (int c = 0; c < D; ++c) a[c] = 0.0f;
+      for (int n = 0; n < N; ++n)
+        for (int c = 0; c < D; ++c) {
           float av = fabsf(src[(int64_t)n * D + c]);
-          if (av > a) a = av;
+          if (av > a[c]) a[c] = av;
         }
-        float s = 0.0f, rcp = 0.0f;
-        if (a > 0.0f) {
-          s = a / 448.0f;
-          rcp = fminf(448.0f / a, FLT_MAX);
+      for (int c = 0; c < D; ++c) {
+        float sc = 0.0f;
+        rcp[c] = 0.0f;
+        if (a[c] > 0.0f) {
+          sc = a[c] / 448.0f;
+          rcp[c] = fminf(448.0f / a[c], FLT_MAX);
         }
-        vscale[((int64_t)b * H + h) * D + c] = s;
-        uint8_t* out = v8t + (((int64_t)b * H + h) * D + c) * (int64_t)npad;
-        for (int n = 0; n < npad; ++n)
-          out[n] = (n < N && a > 0.0f) ? orc_e4m3_encode(src[(int64_t)n * D + c] * rcp) : (uint8_t)0;
+        vscale[((int64_t)b * H + h) * D + c] = sc;
       }
+      for (int n = 0; n < npad; ++n)
+        for (int c = 0; c < D; ++c)
+          out[(int64_t)c * npad + n] =
+              (n < N && a[c] > 0.0f) ? orc_e4m3_encode(src[(int64_t)n * D + c] * rcp[c]) : (uint8_t)0;
     }
+  free(a);
+  free(rcp);
 }
 
 /* v: bf16 [B, N, H, D] strided -> v8t [B, H, D, N_pad], vscale [B, H, D]. */

@@ -1,0 +1,194 @@
+"""Python binding of libqattn (quantized attention forward for MI355X / gfx950).
+
+The functions below carry the C-ABI's names and only marshal arguments: torch tensors'
+device pointers, element strides and the current HIP stream go to ``libqattn.so``;
+every step of the computation runs in the library's HIP kernels.  torch provides the
+device memory and the stream, nothing else.  Importing this package fails loudly when
+the library has not been built (``python -m quantized_attention_qattn_amd._build``);
+there is no fallback.
+
+Layouts (N_pad = ceil(N / 64) * 64):
+  q, k, v   bf16 [B, N, H, D] (any strides with a unit innermost stride)
+  q8, k8    int8 [B, H, N_pad, D];  q_scale, k_scale f32 [B, H, N_pad / 64]
+  k_mean    f32 [B, H, D]
+  v8t       uint8 (e4m3fn codes) [B, H, D, N_pad];  v_scale f32 [B, H, D]
+  out       bf16 or f32 [B, Nq, H, D]
+"""
+from __future__ import annotations
+
+import ctypes as _ct
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqattn.so")
+
+QATTN_OK, QATTN_EINVAL, QATTN_EUNSUPPORTED, QATTN_EWORKSPACE, QATTN_EHIP = 0, -1, -2, -3, -4
+QATTN_OUT_BF16, QATTN_OUT_F32 = 0, 1
+BLOCK = 64
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_attention_qattn_amd._build`")
+
+_lib = _ct.CDLL(LIB_PATH)
+_P, _I, _I64, _F, _SZ = _ct.c_void_p, _ct.c_int, _ct.c_int64, _ct.c_float, _ct.c_size_t
+_I64x3 = _ct.c_int64 * 3
+_I64x2 = _ct.c_int64 * 2
+_lib.qattn_quant_qk.argtypes = [_P, _I64x3, _P, _I64x3, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+_lib.qattn_quant_qk.restype = _I
+_lib.qattn_quant_v.argtypes = [_P, _I64x3, _I, _I, _I, _I, _P, _P, _P]
+_lib.qattn_quant_v.restype = _I
+_lib.qattn_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I64x3, _I, _P]
+_lib.qattn_fwd.restype = _I
+_lib.qattn_fwd_i8kv.argtypes = [_P, _I64x2, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _SZ, _P, _I64x2, _I, _P]
+_lib.qattn_fwd_i8kv.restype = _I
+_lib.qattn_fwd_i8kv_workspace_bytes.argtypes = [_I, _I, _I, _I]
+_lib.qattn_fwd_i8kv_workspace_bytes.restype = _SZ
+_lib.qattn_p8_codes.argtypes = [_P, _P, _I64, _P]
+_lib.qattn_p8_codes.restype = _I
+_lib.qattn_status_string.argtypes = [_I]
+_lib.qattn_status_string.restype = _ct.c_char_p
+
+
+class QattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {qattn_status_string(status)} (status {status})")
+        self.status = status
+
+
+def qattn_status_string(status: int) -> str:
+    return _lib.qattn_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != QATTN_OK:
+        raise QattnError(status, where)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name}: expected a {dtype} CUDA tensor")
+
+
+def npad(n: int) -> int:
+    return (n + BLOCK - 1) // BLOCK * BLOCK
+
+
+# ----------------------------------------------------------------------------------
+# the C-ABI calls (same names, argument marshalling only)
+# ----------------------------------------------------------------------------------
+def qattn_quant_qk(q, k, q8, q_scale, k8, k_scale, k_mean, stream=None) -> None:
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    B, Nq, H, D = q.shape
+    Nk = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
+        raise ValueError("q and k must agree on B, H, D")
+    _check(_lib.qattn_quant_qk(_ptr(q), _I64x3(*q.stride()[:3]), _ptr(k), _I64x3(*k.stride()[:3]), B, H, Nq, Nk, D,
+                               _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(k_mean), _stream(stream)),
+           "qattn_quant_qk")
+
+
+def qattn_quant_v(v, v8t, v_scale, stream=None) -> None:
+    _need(v, torch.bfloat16, "v")
+    B, Nk, H, D = v.shape
+    _check(_lib.qattn_quant_v(_ptr(v), _I64x3(*v.stride()[:3]), B, H, Nk, D, _ptr(v8t), _ptr(v_scale),
+                              _stream(stream)), "qattn_quant_v")
+
+
+def qattn_fwd(q8, q_scale, k8, k_scale, v8t, v_scale, Nq: int, Nk: int, out, scale_log2: float = 0.0,
+              causal: bool = False, stream=None) -> None:
+    B, H, _, D = q8.shape
+    od = QATTN_OUT_BF16 if out.dtype == torch.bfloat16 else QATTN_OUT_F32 if out.dtype == torch.float32 else -1
+    _check(_lib.qattn_fwd(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8t), _ptr(v_scale), B, H, Nq, Nk,
+                          D, float(scale_log2), 1 if causal else 0, _ptr(out), _I64x3(*out.stride()[:3]), od,
+                          _stream(stream)), "qattn_fwd")
+
+
+def qattn_fwd_i8kv_workspace_bytes(H: int, Nq: int, Nk: int, D: int) -> int:
+    return int(_lib.qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D))
+
+
+def qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, workspace, out,
+                   scale_log2: float = 0.0, stream=None) -> None:
+    _need(q, torch.bfloat16, "q")
+    Nq, H, D = q.shape
+    Nk = k_cache.shape[1]
+    od = QATTN_OUT_BF16 if out.dtype == torch.bfloat16 else QATTN_OUT_F32 if out.dtype == torch.float32 else -1
+    _check(_lib.qattn_fwd_i8kv(_ptr(q), _I64x2(*q.stride()[:2]), _ptr(k_cache), _ptr(k_tok_scale), _ptr(v_cache),
+                               _ptr(v_tok_scale), H, Nq, Nk, D, int(pos0), float(scale_log2), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(out), _I64x2(*out.stride()[:2]), od,
+                               _stream(stream)), "qattn_fwd_i8kv")
+
+
+def qattn_p8_codes(u, codes, stream=None) -> None:
+    _need(u, torch.float32, "u")
+    _check(_lib.qattn_p8_codes(_ptr(u), _ptr(codes), u.numel(), _stream(stream)), "qattn_p8_codes")
+
+
+# ----------------------------------------------------------------------------------
+# allocation helpers (torch owns the memory; the library allocates nothing)
+# ----------------------------------------------------------------------------------
+def alloc_qk(B: int, H: int, Nq: int, Nk: int, D: int, device="cuda"):
+    kw = dict(device=device)
+    return dict(
+        q8=torch.empty((B, H, npad(Nq), D), dtype=torch.int8, **kw),
+        q_scale=torch.empty((B, H, npad(Nq) // BLOCK), dtype=torch.float32, **kw),
+        k8=torch.empty((B, H, npad(Nk), D), dtype=torch.int8, **kw),
+        k_scale=torch.empty((B, H, npad(Nk) // BLOCK), dtype=torch.float32, **kw),
+        k_mean=torch.empty((B, H, D), dtype=torch.float32, **kw),
+    )
+
+
+def alloc_v(B: int, H: int, Nk: int, D: int, device="cuda"):
+    return dict(v8t=torch.empty((B, H, D, npad(Nk)), dtype=torch.uint8, device=device),
+                v_scale=torch.empty((B, H, D), dtype=torch.float32, device=device))
+
+
+def quant_qk(q, k, stream=None):
+    B, Nq, H, D = q.shape
+    t = alloc_qk(B, H, Nq, k.shape[1], D, q.device)
+    qattn_quant_qk(q, k, t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["k_mean"], stream)
+    return t
+
+
+def quant_v(v, stream=None):
+    B, Nk, H, D = v.shape
+    t = alloc_v(B, H, Nk, D, v.device)
+    qattn_quant_v(v, t["v8t"], t["v_scale"], stream)
+    return t
+
+
+def attention(q, k, v, causal: bool = False, scale_log2: float = 0.0, out_dtype=torch.bfloat16, stream=None):
+    """Steps 1-5 on bf16 [B, N, H, D] views; returns (out [B, Nq, H, D], intermediates)."""
+    B, Nq, H, D = q.shape
+    qk = quant_qk(q, k, stream)
+    vv = quant_v(v, stream)
+    out = torch.empty((B, Nq, H, D), dtype=out_dtype, device=q.device)
+    qattn_fwd(qk["q8"], qk["q_scale"], qk["k8"], qk["k_scale"], vv["v8t"], vv["v_scale"], Nq, k.shape[1], out,
+              scale_log2, causal, stream)
+    return out, {**qk, **vv}
+
+
+def attention_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, scale_log2: float = 0.0,
+                   out_dtype=torch.bfloat16, stream=None):
+    Nq, H, D = q.shape
+    ws = torch.empty(qattn_fwd_i8kv_workspace_bytes(H, Nq, k_cache.shape[1], D), dtype=torch.uint8, device=q.device)
+    out = torch.empty((Nq, H, D), dtype=out_dtype, device=q.device)
+    qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0, ws, out, scale_log2, stream)
+    return out, ws
+
+
+__all__ = [n for n in dir() if n.startswith("qattn_")] + ["attention", "attention_i8kv", "quant_qk", "quant_v",
+                                                           "alloc_qk", "alloc_v", "QattnError", "LIB_PATH"]

@@ -1,0 +1,358 @@
+// Fused quantized attention forward for gfx950: INT8 MFMA Q.K^T with INT32 accumulation,
+// tile-ordered online softmax with FP8 P, FP8 MFMA P.V, fused V-scale epilogue.
+//
+// Per 64-key tile every query row runs QK -> update m, d, O -> accumulate d -> P to FP8
+// -> PV ("Sage2 SM89 Temporal Pair Experiment", section "Candidate"), so each row's
+// numeric sequence is independent of how rows are grouped into waves.
+//
+// Layout of the work (CDNA4, 64-wide waves):
+//   * a workgroup owns 128 query rows of one (b, h): 4 waves x 32 rows;
+//   * scores are computed transposed, S^T = K . Q^T, with v_mfma_i32_32x32x32_i8: the
+//     accumulator gives each lane one query (its column) and 32 keys of the tile (16 per
+//     32-key block), so the row max and row sum are in-lane plus one exchange with the
+//     lane 32 apart;
+//   * the key order inside a tile is permuted so that lane half h holds keys 32h..32h+31:
+//     K rows are read from LDS through that permutation, so the lane's 32 FP8 P values
+//     are exactly the B operand of v_mfma_f32_32x32x64_f8f6f4 for those 32 keys, and the
+//     A operand (V^T) is a contiguous 32-byte run of the channel-major V tile;
+//   * O^T (D x 32 queries per wave) lives in D/32 accumulators of 16 fp32 per lane;
+//   * K and V^T tiles are staged in LDS (16-byte XOR swizzles against bank conflicts),
+//     the next tile is fetched into registers while the current one is consumed;
+//   * workgroups are mapped so each XCD walks one contiguous range of (b, h, query block)
+//     and keeps the K/V it streams in its own L2.
+#include <climits>
+
+#include "common.h"
+
+namespace qattn {
+namespace detail {
+
+constexpr int BM = 128;  // query rows per workgroup
+[[maybe_unused]] constexpr int BN = 64;   // keys per tile (the numeric contract's tile)
+constexpr int NT = 256;  // threads per workgroup
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9
+// encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+[[maybe_unused]] constexpr int kVmcntZero = 0x0F70;
+
+// P' = 2^fl32(u - 192): the exponent argument on its fixed grid, evaluated with the
+// hardware exponential.  On this grid the e4m3 code of the result equals the code of
+// the correctly rounded power (checked over every fp32 u by qattn_p8_codes).
+__device__ __forceinline__ float p_from_u(float u) { return __builtin_amdgcn_exp2f(u - 192.0f); }
+
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// Physical key (within the tile) of A-operand row m of the QK MFMA for 32-key block kb:
+// the accumulator row m lands in lane half (m >> 2) & 1, register 4 (m >> 3) + (m & 3).
+__device__ __forceinline__ int key_of_row(int kb, int m) {
+  return 32 * ((m >> 2) & 1) + 16 * kb + 4 * (m >> 3) + (m & 3);
+}
+
+// 16-byte-slot swizzles of the LDS tiles (row pitch D bytes for K, 64 bytes for V^T).
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  if (D == 128) return (row & 3) | (((row >> 5) & 1) << 2);
+  return ((row >> 1) & 1) | (((row >> 5) & 1) << 1);
+}
+__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 3; }
+
+template <int D, bool PER_TOKEN, bool CAUSAL>
+__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
+  // The body uses device-only types (buffer resources); the host pass only needs the
+  // kernel's launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NS = D / 32;   // QK k-steps = O accumulator blocks
+  constexpr int KCH = D / 16;  // 16-byte chunks per K row
+  constexpr int PT = D / 64;   // 16-byte chunks per thread per tile (K and V each)
+  // double-buffered tiles: buffer t & 1 holds tile t
+  __shared__ __align__(16) uint8_t sK[2][BN * D];
+  __shared__ __align__(16) uint8_t sV[2][D * BN];
+  __shared__ __align__(16) float sC[2][2][BN];  // PER_TOKEN: c_j per (buffer, query block, key)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int nqb = (a.Nq + BM - 1) / BM;
+  // wave-uniform by construction; readfirstlane lets the compiler keep it in SGPRs
+  const int work = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
+  const int bh = __builtin_amdgcn_readfirstlane(work / nqb);
+  const int qblk = work - bh * nqb;
+  const int q0 = qblk * BM;
+  const int qw = q0 + 32 * wave;  // first row of this wave
+  const int qrow = qw + l32;      // this lane's query row
+  const bool wave_live = qw < a.nq_pad;
+
+  // Q fragment: lane half hh supplies channels [hh*D/2, hh*D/2 + D/2) of its row; QK
+  // step s covers bytes [16 s, 16 s + 16) of that half (the same permutation of the
+  // contraction index is applied to K below, so the INT32 dot products are unchanged).
+  v4i qf[NS];
+  if (wave_live) {
+    const int8_t* qp = a.q8 + bh * a.q8_bh + (int64_t)qrow * D + hh * (D / 2);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = *(const v4i*)(qp + 16 * s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = v4i{0, 0, 0, 0};
+  }
+  const float sq_w = wave_live ? a.q_scale[bh * a.qs_bh + qw / kBlk] : 0.0f;
+  float sq_blk[2] = {0.0f, 0.0f};
+  if (PER_TOKEN) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (q0 + kBlk * i < a.nq_pad) sq_blk[i] = a.q_scale[bh * a.qs_bh + q0 / kBlk + i];
+  }
+
+  int ntiles = (a.Nk + BN - 1) / BN;
+  if (CAUSAL) {
+    int64_t last = (int64_t)min(q0 + BM, a.Nq) - 1 + a.pos_off;
+    if (last > a.Nk - 1) last = a.Nk - 1;
+    ntiles = last < 0 ? 0 : (int)(last / BN) + 1;
+  }
+
+  // ---- staging: global -> LDS directly (buffer loads with the LDS destination) ----
+  // Each wave fills PT 1 KiB segments of the K tile and of the V^T tile; lane l of a
+  // segment writes LDS slot 64 seg + l (16 bytes), so each lane fetches the global chunk
+  // that the swizzled layout keeps in that slot.  Buffer resources are per (b, h) with
+  // 32-bit offsets; rows past the end of the resource (a KV cache whose length is not a
+  // multiple of 64) read as zeros.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(a.k8 + bh * a.k8_bh), (short)0, a.k_rows * D, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(a.v8t + bh * a.v8t_bh), (short)0, (int)(D * a.ldv), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)uniform_ptr(a.k_scale + bh * a.ks_bh), (short)0, PER_TOKEN ? a.Nk * 4 : 0, kRsrcWord3);
+  int koff[PT], voff[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int slot = 64 * (wave * PT + i) + lane;
+    const int row = slot / KCH, pc = slot % KCH;
+    koff[i] = row * D + 16 * (pc ^ kswz<D>(row));
+    const int vrow = slot >> 2, vpc = slot & 3;
+    voff[i] = vrow * (int)a.ldv + 16 * (vpc ^ vswz(vrow));
+  }
+  auto stage = [&](int t) {
+    const int buf = t & 1;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int seg = wave * PT + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(&sK[buf][1024 * seg]),
+                                               16, koff[i], t * BN * D, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(&sV[buf][1024 * seg]),
+                                               16, voff[i], t * BN, 0, 0);
+    }
+  };
+  float cr = 0.0f;
+  auto scale_load = [&](int t) {
+    if (PER_TOKEN && tid < 2 * BN) {
+      const float sk =
+          __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 4 * (tid & (BN - 1)), 4 * t * BN, 0));
+      cr = (sq_blk[tid / BN] * sk) * a.lambda;
+    }
+  };
+  auto scale_store = [&](int t) {
+    if (PER_TOKEN && tid < 2 * BN) sC[t & 1][tid / BN][tid & (BN - 1)] = cr;
+  };
+
+  float m = -INFINITY;  // running max (log2 domain)
+  float dsum = 0.0f;    // this lane's share of d' (its 32 keys of every tile)
+  v16f O[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) O[s][r] = 0.0f;
+
+  if (ntiles > 0) {
+    stage(0);
+    scale_load(0);
+    scale_store(0);
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __syncthreads();
+
+  const int krow0 = key_of_row(0, l32), krow1 = key_of_row(1, l32);
+  for (int t = 0; t < ntiles; ++t) {
+    const bool nxt = t + 1 < ntiles;
+    // buffer (t+1)&1 was last read in iteration t-1, which ended with a barrier
+    if (nxt) {
+      stage(t + 1);
+      scale_load(t + 1);
+    }
+    const uint8_t* tK = sK[t & 1];
+    const uint8_t* tV = sV[t & 1];
+
+    // ---- QK: S^T for keys of block 0 and block 1 ----
+    v16i S0, S1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      S0[r] = 0;
+      S1[r] = 0;
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int ch = NS * hh + s;
+      const v4i k0 = *(const v4i*)(tK + krow0 * D + 16 * (ch ^ kswz<D>(krow0)));
+      S0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qf[s], S0, 0, 0, 0);
+      const v4i k1 = *(const v4i*)(tK + krow1 * D + 16 * (ch ^ kswz<D>(krow1)));
+      S1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qf[s], S1, 0, 0, 0);
+    }
+
+    // ---- online softmax over this lane's 32 keys (key 32 hh + i, i = 16 kb + j) ----
+    const int64_t key0 = (int64_t)t * BN + 32 * hh;
+    const bool masked = ((int64_t)t * BN + BN > a.Nk) || (CAUSAL && (int64_t)t * BN + BN - 1 > (int64_t)qw + a.pos_off);
+    const int64_t vis_last = CAUSAL ? min((int64_t)qrow + a.pos_off, (int64_t)a.Nk - 1) : (int64_t)a.Nk - 1;
+    float cvec[32];
+    float c_tile = 0.0f;
+    float Mt;
+    if (PER_TOKEN) {
+      const float* cp = &sC[t & 1][wave >> 1][32 * hh];
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const float4 c4 = *(const float4*)(cp + i);
+        cvec[i] = c4.x;
+        cvec[i + 1] = c4.y;
+        cvec[i + 2] = c4.z;
+        cvec[i + 3] = c4.w;
+      }
+      Mt = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int acc = i < 16 ? S0[i] : S1[i - 16];
+        const float sv = (float)acc * cvec[i];
+        const bool vis = !masked || (key0 + i <= vis_last);
+        Mt = vis ? fmaxf(Mt, sv) : Mt;
+      }
+      Mt = fmaxf(Mt, __shfl_xor(Mt, 32, 64));
+    } else {
+      c_tile = (sq_w * a.k_scale[bh * a.ks_bh + t]) * a.lambda;
+      int mx = INT_MIN;
+      if (!masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = max(mx, max(S0[i], S1[i]));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int acc = i < 16 ? S0[i] : S1[i - 16];
+          mx = (key0 + i <= vis_last) ? max(mx, acc) : mx;
+        }
+      }
+      mx = max(mx, __shfl_xor(mx, 32, 64));
+      Mt = mx == INT_MIN ? -INFINITY : (float)mx * c_tile;
+    }
+    const float mnew = fmaxf(m, Mt);
+    const float ms = mnew == -INFINITY ? 0.0f : mnew;
+    const bool same = mnew == m;
+    const float alpha = same ? 1.0f : __builtin_amdgcn_exp2f(m - ms);
+    const float bconst = 200.0f - ms;
+    dsum *= alpha;
+
+    v8i pf;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * w + e;
+        const int acc = i < 16 ? S0[i] : S1[i - 16];
+        const float cc = PER_TOKEN ? cvec[i] : c_tile;
+        float pv = p_from_u(__builtin_fmaf((float)acc, cc, bconst));
+        if (masked) pv = (key0 + i <= vis_last) ? pv : 0.0f;
+        dsum += pv;
+        p[e] = pv;
+      }
+      pf[w] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+    }
+    if (__ballot(!same) != 0) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[s][r] *= alpha;
+    }
+    m = mnew;
+
+    // ---- PV: O^T[32 channels x 32 queries] += V^T[channels x 64 keys] . P^T ----
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int vrow = 32 * s + l32;
+      const v4i va = *(const v4i*)(tV + vrow * BN + 16 * ((2 * hh) ^ vswz(vrow)));
+      const v4i vb = *(const v4i*)(tV + vrow * BN + 16 * ((2 * hh + 1) ^ vswz(vrow)));
+      const v8i vf = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+      O[s] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, O[s], 0, 0, 0, 127, 0, 127);
+    }
+
+    if (nxt) scale_store(t + 1);
+    // own LDS-bound loads of tile t+1 complete, then everyone's (and tile t is consumed)
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
+    __syncthreads();
+  }
+
+  // ---- epilogue: out = O * s_v / d' ----
+  const float dt = dsum + __shfl_xor(dsum, 32, 64);
+  if (qrow < a.Nq) {
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int64_t off = b * a.out_sb + (int64_t)qrow * a.out_sn + h * a.out_sh;
+    const float* vs = a.v_scale + (int64_t)bh * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c0 = 32 * s + 8 * g + 4 * hh;  // channels c0 .. c0 + 3
+        float o[4];
+        const float svv[4] = {vs[c0], vs[c0 + 1], vs[c0 + 2], vs[c0 + 3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = dt == 0.0f ? 0.0f : (O[s][4 * g + e] * svv[e]) / dt;
+        if (a.out_bf16) {
+          uint16_t* op = (uint16_t*)a.out + off + c0;
+          const uint32_t w0 = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+          const uint32_t w1 = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+          *(uint2*)op = make_uint2(w0, w1);
+        } else {
+          float* op = (float*)a.out + off + c0;
+          *(float4*)op = make_float4(o[0], o[1], o[2], o[3]);
+        }
+      }
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+__global__ void p8_codes_kernel(const float* u, uint8_t* codes, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    codes[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(p_from_u(u[i]), 0.0f, 0, false) & 0xff);
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
+  const int nqb = (a.Nq + BM - 1) / BM;
+  const int grid = a.B * a.H * nqb;
+  if (a.per_token) {
+    if (a.causal)
+      attn_fwd_kernel<D, true, true><<<grid, NT, 0, st>>>(a);
+    else
+      attn_fwd_kernel<D, true, false><<<grid, NT, 0, st>>>(a);
+  } else {
+    if (a.causal)
+      attn_fwd_kernel<D, false, true><<<grid, NT, 0, st>>>(a);
+    else
+      attn_fwd_kernel<D, false, false><<<grid, NT, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace detail
+using namespace detail;
+
+hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st) {
+  return D == 128 ? launch_d<128>(a, st) : launch_d<64>(a, st);
+}
+
+hipError_t launch_p8_codes(const float* u, uint8_t* codes, int64_t n, hipStream_t st) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  p8_codes_kernel<<<(int)blocks, 256, 0, st>>>(u, codes, n);
+  return hipGetLastError();
+}
+
+}  // namespace qattn

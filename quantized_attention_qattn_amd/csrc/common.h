@@ -1,0 +1,93 @@
+// Internal device helpers and launcher declarations for libqattn (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qattn {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kBlk = 64;  // rows per Q/K scale block, keys per KV tile
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs: 32-bit data format,
+// bounds checked against num_records (out-of-range loads return zero).
+constexpr int kRsrcWord3 = 0x00020000;
+
+// A wave-uniform pointer moved to scalar registers (both halves via readfirstlane), so
+// buffer resources built from it need no per-lane waterfall.
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Unpack 8 bf16 values held in a 16-byte vector into fp32 (exact).
+__device__ __forceinline__ void unpack_bf16x8(const v4i& w, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo((uint32_t)w[i]);
+    f[2 * i + 1] = bf16_hi((uint32_t)w[i]);
+  }
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Workgroup id -> work item so that each of the 8 XCDs (workgroups are dealt to XCDs
+// round-robin by id) receives one contiguous range of work items.  Neighbouring work
+// items share K/V, so the K/V tiles they stream stay in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  constexpr int X = 8;
+  const int x = id % X, slot = id / X;
+  const int q = n / X, r = n % X;
+  return x * q + (x < r ? x : r) + slot;
+}
+
+// ---------------------------------------------------------------------------------
+// launchers (defined in quant.hip / attn_fwd.hip); all asynchronous on `st`
+// ---------------------------------------------------------------------------------
+struct BshdView {
+  const void* p;
+  int64_t sb, sn, sh;  // element strides; d stride is 1
+};
+
+hipError_t launch_k_mean(BshdView k, int B, int H, int N, int D, int npad, int8_t* scratch, float* mean,
+                         hipStream_t st);
+hipError_t launch_quant_i8(BshdView x, const float* mean, int B, int H, int N, int D, int npad, int8_t* codes,
+                           float* scales, hipStream_t st);
+// V: bf16 view (cache == nullptr) or int8 cache [H, N, D] with per-token scales (B must be 1)
+hipError_t launch_quant_v(BshdView v, const int8_t* cache, const float* tok_scale, int B, int H, int N, int D,
+                          int npad, uint8_t* v8t, float* v_scale, hipStream_t st);
+
+struct FwdArgs {
+  const int8_t* q8;
+  const float* q_scale;
+  const int8_t* k8;
+  const float* k_scale;
+  const uint8_t* v8t;
+  const float* v_scale;
+  void* out;
+  int64_t q8_bh, qs_bh, k8_bh, ks_bh, v8t_bh, ldv;  // per-(b,h) element strides
+  int64_t out_sb, out_sn, out_sh;
+  int B, H, Nq, Nk, nq_pad, k_rows;
+  float lambda;
+  int64_t pos_off;  // causal: key j visible to query i iff j <= i + pos_off
+  int causal, per_token, out_bf16;
+};
+hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st);
+hipError_t launch_p8_codes(const float* u, uint8_t* codes, int64_t n, hipStream_t st);
+
+}  // namespace qattn

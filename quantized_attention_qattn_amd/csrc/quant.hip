@@ -1,0 +1,304 @@
+// Preparation kernels: K channel mean, INT8 per-64-row blocks of Q and smoothed K, and
+// per-channel e4m3 V written channel-major ("H3 Performance Roadmap", "Measured GB10
+// Baseline": K smoothing, Q/K INT8 quantization, V transpose + FP8 quantization;
+// "Phase 4" items 2-3).  All of them stream their input once or twice from HBM; each
+// thread moves 16-byte vectors, workgroups cover 64-row blocks or 256-token chunks.
+#include "common.h"
+
+namespace qattn {
+namespace detail {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 256;  // tokens per partial-reduction workgroup
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------------------------
+// a1: K channel mean.  Pass 1 sums each 256-token chunk in fp64 (the sum of bf16 values
+// is exact in fp64 for these magnitudes, so the order is immaterial) into scratch that
+// lives in the k8 region of the same (b, h); pass 2 adds the chunks and divides once.
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_mean_partial(BshdView k, int H, int N, int64_t region, int8_t* scratch) {
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int RPP = kThreads / CPR;  // rows per pass
+  __shared__ double red[RPP][D];
+  const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n0 = chunk * kChunk, n1 = min(N, n0 + kChunk);
+  const uint16_t* base = (const uint16_t*)k.p + b * k.sb + h * k.sh + cg * 8;
+  double acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  for (int n = n0 + rl; n < n1; n += RPP) {
+    v4i w = *(const v4i*)(base + (int64_t)n * k.sn);
+    float f[8];
+    unpack_bf16x8(w, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += (double)f[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rl][cg * 8 + i] = acc[i];
+  __syncthreads();
+  if (t < D) {
+    double s = 0.0;
+    for (int r = 0; r < RPP; ++r) s += red[r][t];
+    double* part = (double*)(scratch + (int64_t)(b * H + h) * region);
+    part[chunk * D + t] = s;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void k_mean_final(int N, int nchunk, int64_t region, const int8_t* scratch, float* mean) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const double* part = (const double*)(scratch + (int64_t)bh * region);
+  double s = 0.0;
+  for (int i = 0; i < nchunk; ++i) s += part[i * D + c];
+  mean[(int64_t)bh * D + c] = (float)(s / (double)N);
+}
+
+// ---------------------------------------------------------------------------------
+// a2: INT8 blocks of 64 rows: a = max|x|, s = a/127, code = rne(x * min(127/a, FLT_MAX)).
+// One workgroup per (block, h, b); each thread keeps its 8-channel slices in registers.
+// ---------------------------------------------------------------------------------
+template <int D, bool SMOOTH>
+__global__ __launch_bounds__(kThreads) void quant_i8_blocks(BshdView x, const float* mean, int H, int N, int npad,
+                                                            int8_t* codes, float* scales) {
+  constexpr int CPR = D / 8, RPP = kThreads / CPR, PASSES = kBlk / RPP;
+  __shared__ float wmax[kThreads / 64];
+  const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int r0 = blk * kBlk;
+  const int64_t bh = (int64_t)b * H + h;
+  const uint16_t* base = (const uint16_t*)x.p + b * x.sb + h * x.sh + cg * 8;
+  float mu[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mu[i] = SMOOTH ? mean[bh * D + cg * 8 + i] : 0.0f;
+  float v[PASSES][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int n = r0 + rl + p * RPP;
+    if (n < N) {
+      v4i w = *(const v4i*)(base + (int64_t)n * x.sn);
+      float f[8];
+      unpack_bf16x8(w, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[p][i] = SMOOTH ? f[i] - mu[i] : f[i];
+        amax = fmaxf(amax, fabsf(v[p][i]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[p][i] = 0.0f;
+    }
+  }
+  amax = wave_max(amax);
+  if ((t & 63) == 0) wmax[t >> 6] = amax;
+  __syncthreads();
+  float a = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) a = fmaxf(a, wmax[w]);
+  float s = 0.0f, r = 0.0f;
+  if (a > 0.0f) {
+    s = a / 127.0f;
+    r = fminf(127.0f / a, kFltMax);
+  }
+  if (t == 0) scales[bh * (npad / kBlk) + blk] = s;
+  int8_t* out = codes + (bh * npad + r0) * D + cg * 8;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q = __builtin_rintf(v[p][i] * r);
+      q = fminf(fmaxf(q, -127.0f), 127.0f);
+      wd[i >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (i & 3));
+    }
+    *(uint2*)(out + (int64_t)(rl + p * RPP) * D) = make_uint2(wd[0], wd[1]);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// a3: per-channel e4m3 V.  Pass 1: per-chunk channel absmax into scratch inside v8t;
+// pass 2: the channel absmax is parked in v_scale; pass 3: encode 64-token tiles and
+// write them channel-major through an LDS transpose; pass 4: v_scale = absmax / 448.
+// The input is either a bf16 view or an int8 cache with per-token scales, dequantized
+// as fl32(code * scale).
+// ---------------------------------------------------------------------------------
+template <int D, bool CACHE>
+__device__ __forceinline__ void load_v8(BshdView v, const int8_t* cache, const float* tok_scale, int b, int h, int H,
+                                        int N, int n, int cg, float (&f)[8]) {
+  if (CACHE) {
+    const int8_t* row = cache + ((int64_t)h * N + n) * D + cg * 8;
+    uint2 w = *(const uint2*)row;
+    const float sc = tok_scale[(int64_t)h * N + n];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = (float)(int8_t)(w.x >> (8 * i)) * sc;
+      f[4 + i] = (float)(int8_t)(w.y >> (8 * i)) * sc;
+    }
+  } else {
+    v4i w = *(const v4i*)((const uint16_t*)v.p + b * v.sb + (int64_t)n * v.sn + h * v.sh + cg * 8);
+    unpack_bf16x8(w, f);
+  }
+}
+
+template <int D, bool CACHE>
+__global__ __launch_bounds__(kThreads) void v_amax_partial(BshdView v, const int8_t* cache, const float* tok_scale,
+                                                           int H, int N, int64_t region, uint8_t* scratch) {
+  constexpr int CPR = D / 8, RPP = kThreads / CPR;
+  __shared__ float red[RPP][D];
+  const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n0 = chunk * kChunk, n1 = min(N, n0 + kChunk);
+  float mx[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx[i] = 0.0f;
+  for (int n = n0 + rl; n < n1; n += RPP) {
+    float f[8];
+    load_v8<D, CACHE>(v, cache, tok_scale, b, h, H, N, n, cg, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(f[i]));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rl][cg * 8 + i] = mx[i];
+  __syncthreads();
+  if (t < D) {
+    float m = 0.0f;
+    for (int r = 0; r < RPP; ++r) m = fmaxf(m, red[r][t]);
+    float* part = (float*)(scratch + ((int64_t)b * H + h) * region);
+    part[chunk * D + t] = m;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void v_amax_final(int nchunk, int64_t region, const uint8_t* scratch, float* v_scale) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const float* part = (const float*)(scratch + (int64_t)bh * region);
+  float m = 0.0f;
+  for (int i = 0; i < nchunk; ++i) m = fmaxf(m, part[i * D + c]);
+  v_scale[(int64_t)bh * D + c] = m;  // the absmax; converted to the scale after encoding
+}
+
+template <int D, bool CACHE>
+__global__ __launch_bounds__(kThreads) void v_encode(BshdView v, const int8_t* cache, const float* tok_scale, int H,
+                                                     int N, int npad, const float* v_amax, uint8_t* v8t) {
+  constexpr int CPR = D / 8, RPP = kThreads / CPR, PASSES = kBlk / RPP;
+  constexpr int PITCH = kBlk + 16;  // transpose buffer row pitch (bytes)
+  __shared__ __align__(16) uint8_t sT[D * PITCH];
+  const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = (int64_t)b * H + h;
+  const int n0 = tile * kBlk;
+  float rc[8];
+  bool zc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = v_amax[bh * D + cg * 8 + i];
+    zc[i] = !(a > 0.0f);
+    rc[i] = zc[i] ? 0.0f : fminf(448.0f / a, kFltMax);
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int nl = rl + p * RPP, n = n0 + nl;
+    float f[8];
+    if (n < N) {
+      load_v8<D, CACHE>(v, cache, tok_scale, b, h, H, N, n, cg, f);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      // hardware e4m3 conversion: round to nearest even; |f * r| <= 448 (1 + 2^-23)
+      uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[i] * rc[i], f[i + 1] * rc[i + 1], 0, false);
+      uint32_t c0 = (zc[i] || n >= N) ? 0u : (w & 0xffu);
+      uint32_t c1 = (zc[i + 1] || n >= N) ? 0u : ((w >> 8) & 0xffu);
+      sT[(cg * 8 + i) * PITCH + nl] = (uint8_t)c0;
+      sT[(cg * 8 + i + 1) * PITCH + nl] = (uint8_t)c1;
+    }
+  }
+  __syncthreads();
+  constexpr int CHUNKS = D * (kBlk / 16);
+  for (int id = t; id < CHUNKS; id += kThreads) {
+    const int c = id >> 2, part = id & 3;
+    *(v4i*)(v8t + (bh * D + c) * npad + n0 + 16 * part) = *(const v4i*)(sT + c * PITCH + 16 * part);
+  }
+}
+
+__global__ void v_scale_from_amax(float* v_scale, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) v_scale[i] = v_scale[i] / 448.0f;
+}
+
+inline int nchunks(int N) { return (N + kChunk - 1) / kChunk; }
+
+}  // namespace detail
+using namespace detail;
+
+hipError_t launch_k_mean(BshdView k, int B, int H, int N, int D, int npad, int8_t* scratch, float* mean,
+                         hipStream_t st) {
+  const int64_t region = (int64_t)npad * D;  // bytes of k8 per (b, h)
+  const int nc = nchunks(N);
+  dim3 g1(nc, H, B);
+  if (D == 128) {
+    k_mean_partial<128><<<g1, kThreads, 0, st>>>(k, H, N, region, scratch);
+    k_mean_final<128><<<B * H, 128, 0, st>>>(N, nc, region, scratch, mean);
+  } else {
+    k_mean_partial<64><<<g1, kThreads, 0, st>>>(k, H, N, region, scratch);
+    k_mean_final<64><<<B * H, 64, 0, st>>>(N, nc, region, scratch, mean);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_i8(BshdView x, const float* mean, int B, int H, int N, int D, int npad, int8_t* codes,
+                           float* scales, hipStream_t st) {
+  dim3 g(npad / kBlk, H, B);
+  if (D == 128) {
+    if (mean)
+      quant_i8_blocks<128, true><<<g, kThreads, 0, st>>>(x, mean, H, N, npad, codes, scales);
+    else
+      quant_i8_blocks<128, false><<<g, kThreads, 0, st>>>(x, mean, H, N, npad, codes, scales);
+  } else {
+    if (mean)
+      quant_i8_blocks<64, true><<<g, kThreads, 0, st>>>(x, mean, H, N, npad, codes, scales);
+    else
+      quant_i8_blocks<64, false><<<g, kThreads, 0, st>>>(x, mean, H, N, npad, codes, scales);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool CACHE>
+static void quant_v_impl(BshdView v, const int8_t* cache, const float* tok_scale, int B, int H, int N, int npad,
+                         uint8_t* v8t, float* v_scale, hipStream_t st) {
+  const int64_t region = (int64_t)npad * D;  // bytes of v8t per (b, h)
+  const int nc = nchunks(N);
+  v_amax_partial<D, CACHE><<<dim3(nc, H, B), kThreads, 0, st>>>(v, cache, tok_scale, H, N, region, v8t);
+  v_amax_final<D><<<B * H, D, 0, st>>>(nc, region, v8t, v_scale);
+  v_encode<D, CACHE><<<dim3(npad / kBlk, H, B), kThreads, 0, st>>>(v, cache, tok_scale, H, N, npad, v_scale, v8t);
+  const int64_t n = (int64_t)B * H * D;
+  v_scale_from_amax<<<(int)((n + 255) / 256), 256, 0, st>>>(v_scale, n);
+}
+
+hipError_t launch_quant_v(BshdView v, const int8_t* cache, const float* tok_scale, int B, int H, int N, int D,
+                          int npad, uint8_t* v8t, float* v_scale, hipStream_t st) {
+  if (D == 128) {
+    if (cache)
+      quant_v_impl<128, true>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, st);
+    else
+      quant_v_impl<128, false>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, st);
+  } else {
+    if (cache)
+      quant_v_impl<64, true>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, st);
+    else
+      quant_v_impl<64, false>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qattn

@@ -1,0 +1,344 @@
+"""GPU parity: the HIP path (through the C-ABI binding) against the CPU oracle.
+
+* codes and scales (q8, k8, v8t, their scales, the K mean, the prefill workspace) are
+  compared bit for bit;
+* attention outputs (fp32) must satisfy max|gpu - oracle| <= 2e-3 * RMS(oracle); bf16
+  outputs must be the round-to-nearest-even of the GPU's own fp32 result;
+* full-size workloads are checked on sampled query blocks (rows are independent).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def qa():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import quantized_attention_qattn_amd as qa
+
+    oracle.build(force=False)
+    return qa
+
+
+def dev_bf16(u16: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt((ref ** 2).mean())
+    err = np.abs(gpu - ref).max()
+    assert np.isfinite(gpu).all(), what
+    assert err <= TOL * rms, f"{what}: max abs err {err:.3e} > {TOL} * rms {rms:.3e} (ratio {err / rms:.2e})"
+    return err / rms
+
+
+def bf16_of(f32: np.ndarray) -> np.ndarray:
+    return W.bf16_bits(f32)
+
+
+# ----------------------------------------------------------------------------------
+# preparation: bit-exact
+# ----------------------------------------------------------------------------------
+QK_SHAPES = [(1, 2, 256, 256, 64), (2, 3, 150, 77, 128), (1, 1, 1, 1, 64), (1, 2, 65, 300, 128), (1, 1, 700, 1100, 64)]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,D", QK_SHAPES)
+def test_quant_qk_bit_exact(qa, B, H, Nq, Nk, D):
+    say(f"quant_qk B={B} H={H} Nq={Nq} Nk={Nk} D={D}")
+    rng = np.random.default_rng(100 + Nq + Nk + D)
+    q = W.bf16_bits(rng.standard_normal((B, Nq, H, D)).astype(np.float32) * 3)
+    k = W.bf16_bits(rng.standard_normal((B, Nk, H, D)).astype(np.float32) + rng.uniform(-2, 2, (B, 1, H, D)).astype(np.float32))
+    t = qa.quant_qk(dev_bf16(q), dev_bf16(k))
+    torch.cuda.synchronize()
+    q8, qs, k8, ks, mean = oracle.quant_qk(q, k)
+    assert np.array_equal(host(t["k_mean"]), mean)
+    assert np.array_equal(host(t["q8"]), q8)
+    assert np.array_equal(host(t["q_scale"]).view(np.uint32), qs.view(np.uint32))
+    assert np.array_equal(host(t["k8"]), k8)
+    assert np.array_equal(host(t["k_scale"]).view(np.uint32), ks.view(np.uint32))
+
+
+def test_quant_qk_strided_views(qa):
+    """Q and K as projection-strided views of one packed [B, N, 3, H, D] tensor."""
+    say("quant_qk strided views")
+    rng = np.random.default_rng(7)
+    B, N, H, D = 2, 130, 4, 128
+    qkv = W.bf16_bits(rng.standard_normal((B, N, 3, H, D)).astype(np.float32))
+    dq = dev_bf16(qkv)
+    t = qa.quant_qk(dq[:, :, 0], dq[:, :, 1])
+    torch.cuda.synchronize()
+    q8, qs, k8, ks, mean = oracle.quant_qk(qkv[:, :, 0], qkv[:, :, 1])
+    assert np.array_equal(host(t["q8"]), q8) and np.array_equal(host(t["k8"]), k8)
+    assert np.array_equal(host(t["k_mean"]), mean) and np.array_equal(host(t["k_scale"]), ks)
+    v = qa.quant_v(dq[:, :, 2])
+    torch.cuda.synchronize()
+    v8t, vs = oracle.quant_v(qkv[:, :, 2])
+    assert np.array_equal(host(v["v8t"]), v8t) and np.array_equal(host(v["v_scale"]), vs)
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,D", QK_SHAPES)
+def test_quant_v_bit_exact(qa, B, H, Nq, Nk, D):
+    say(f"quant_v B={B} H={H} Nk={Nk} D={D}")
+    rng = np.random.default_rng(200 + Nk + D)
+    v = W.bf16_bits(rng.standard_normal((B, Nk, H, D)).astype(np.float32) * np.exp2(rng.uniform(-3, 3, (1, 1, H, D))).astype(np.float32))
+    v[:, :, 0, 1] = 0  # a zero channel
+    t = qa.quant_v(dev_bf16(v))
+    torch.cuda.synchronize()
+    v8t, vs = oracle.quant_v(v)
+    assert np.array_equal(host(t["v8t"]), v8t)
+    assert np.array_equal(host(t["v_scale"]).view(np.uint32), vs.view(np.uint32))
+
+
+def test_quant_v_every_bf16_value(qa):
+    """Channel 0 holds every bf16 value with |v| <= 448 (amax 448, so fl32(v * 1) is
+    encoded as is): the GPU's e4m3 encoder must match the oracle's on all of them."""
+    say("quant_v every bf16 value")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = W.bf16_to_f32(bits)
+    vals = bits[np.isfinite(f) & (np.abs(f) <= 448.0)]
+    N = len(vals)
+    rng = np.random.default_rng(3)
+    v = W.bf16_bits(rng.standard_normal((1, N, 1, 64)).astype(np.float32))
+    v[0, :, 0, 0] = vals
+    t = qa.quant_v(dev_bf16(v))
+    torch.cuda.synchronize()
+    v8t, vs = oracle.quant_v(v)
+    assert vs[0, 0, 0] == 1.0
+    assert np.array_equal(host(t["v8t"]), v8t)
+
+
+def test_p8_codes_whole_grid(qa):
+    """The fused kernel's P8 code of 2^(u - 192) for EVERY fp32 u in [64, 384) equals the
+    code of the correctly rounded power (the oracle's)."""
+    lo = int(np.float32(64.0).view(np.uint32))
+    hi = int(np.float32(384.0).view(np.uint32))
+    say(f"p8 codes over {hi - lo} grid arguments")
+    u = torch.arange(lo, hi, dtype=torch.int64, device="cuda").to(torch.int32).view(torch.float32)
+    codes = torch.empty(hi - lo, dtype=torch.uint8, device="cuda")
+    qa.qattn_p8_codes(u, codes)
+    torch.cuda.synchronize()
+    ref = oracle.p8_codes_grid(lo, hi)
+    got = host(codes)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, f"{bad.size} mismatches, first u bits {[hex(lo + int(i)) for i in bad[:5]]}"
+
+
+# ----------------------------------------------------------------------------------
+# fused loop
+# ----------------------------------------------------------------------------------
+def run_fwd(qa, ops, Nq, Nk, lam, causal, out_dtype=torch.float32):
+    q8, qs, k8, ks, v8t, vs = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in ops]
+    B, H, _, D = q8.shape
+    out = torch.empty((B, Nq, H, D), dtype=out_dtype, device="cuda")
+    qa.qattn_fwd(q8, qs, k8, ks, v8t, vs, Nq, Nk, out, lam, causal)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def test_fwd_tiny_workload(qa):
+    w = W.TINY
+    say(f"fwd {w.name}")
+    q, k, v = W.dense_inputs(w)
+    out32, inter = qa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), out_dtype=torch.float32)
+    out16, _ = qa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, it = oracle.fwd(q, k, v)
+    assert np.array_equal(host(inter["q8"]), it["q8"]) and np.array_equal(host(inter["v8t"]), it["v8t"])
+    r = assert_close(host(out32), ref, w.name)
+    say(f"  max err / rms = {r:.2e}")
+    assert np.array_equal(host(out16), bf16_of(host(out32)))
+
+
+def _exact_ops(rng, Nq, Nk, D, H=2):
+    """Operands whose scores are small integers (see the oracle's exact pins)."""
+    npq, npk = oracle.npad(Nq), oracle.npad(Nk)
+    qs = rng.choice(np.float32([1.0, 2.0]), (1, H, npq // 64)).astype(np.float32)
+    ks = rng.choice(np.float32([1.0, 0.5]), (1, H, npk // 64)).astype(np.float32)
+    q8 = np.zeros((1, H, npq, D), np.int8)
+    for h in range(H):
+        q8[0, h, np.arange(Nq), rng.integers(0, D, Nq)] = 1
+    k8 = np.zeros((1, H, npk, D), np.int8)
+    for h in range(H):
+        for kb in range(npk // 64):
+            vals = np.int8([-1, 0]) if ks[0, h, kb] == 1.0 else np.int8([-2, 0])
+            k8[0, h, kb * 64:(kb + 1) * 64] = rng.choice(vals, (64, D))
+    k8[0, :, Nk:] = 0
+    codes = oracle.e4m3_encode(np.float32([1, 1.5, 2, 3, -1, -1.5, -2, -3]))
+    v8t = np.zeros((1, H, D, npk), np.uint8)
+    v8t[..., :Nk] = codes[rng.integers(0, 8, (1, H, D, Nk))]
+    vs = np.exp2(-rng.integers(0, 4, (1, H, D))).astype(np.float32)
+    return q8, qs, k8, ks, v8t, vs
+
+
+SHAPES = [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_exact_tile_boundary_shapes(qa, D, causal):
+    """1-4-tile boundary shapes with exact scores: GPU == oracle within 2 ulp."""
+    rng = np.random.default_rng(1000 + D + causal)
+    for Nk in SHAPES:
+        for Nq in [1, 63, 65, 129, 256]:
+            if causal and Nq > Nk:
+                continue
+            say(f"exact Nq={Nq} Nk={Nk} D={D} causal={causal}")
+            ops = _exact_ops(rng, Nq, Nk, D)
+            got = run_fwd(qa, ops, Nq, Nk, 1.0, causal)
+            ref = oracle.attn(*ops, Nq, Nk, 1.0, causal=causal)
+            ulp = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+            assert ulp.max() <= 2, (Nq, Nk, D, causal, ulp.max())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_random_tile_shapes(qa, D, causal):
+    rng = np.random.default_rng(2000 + D + causal)
+    for Nq, Nk in [(1, 1), (65, 129), (193, 256), (127, 63), (300, 555), (64, 1000)]:
+        if causal and Nq > Nk:
+            Nq, Nk = Nk, Nq
+        say(f"random Nq={Nq} Nk={Nk} D={D} causal={causal}")
+        q = W.bf16_bits(rng.standard_normal((1, Nq, 3, D)).astype(np.float32))
+        k = W.bf16_bits(rng.standard_normal((1, Nk, 3, D)).astype(np.float32) + 1)
+        v = W.bf16_bits(rng.standard_normal((1, Nk, 3, D)).astype(np.float32))
+        out, _ = qa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=causal, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        ref, _ = oracle.fwd(q, k, v, causal=causal)
+        assert_close(host(out), ref, f"Nq={Nq} Nk={Nk}")
+
+
+def test_fwd_causal_fully_masked_rows(qa):
+    say("causal Nq > Nk")
+    rng = np.random.default_rng(5)
+    Nq, Nk, D = 200, 70, 64
+    q = W.bf16_bits(rng.standard_normal((1, Nq, 2, D)).astype(np.float32))
+    k = W.bf16_bits(rng.standard_normal((1, Nk, 2, D)).astype(np.float32))
+    v = W.bf16_bits(rng.standard_normal((1, Nk, 2, D)).astype(np.float32))
+    out, _ = qa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, _ = oracle.fwd(q, k, v, causal=True)
+    o = host(out)
+    assert not o[:, : Nq - Nk].any()
+    assert_close(o, ref, "causal Nq>Nk")
+
+
+def test_fwd_deterministic_and_stream(qa):
+    say("determinism + side stream")
+    w = W.TINY
+    q, k, v = W.dense_inputs(w)
+    a, _ = qa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b, _ = qa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a), host(b))
+
+
+def test_i8kv_small(qa):
+    say("i8kv small")
+    rng = np.random.default_rng(60)
+    for H, D, Nq, Nk, pos0 in [(2, 128, 100, 700, 600), (3, 64, 64, 64, 0), (2, 128, 1, 129, 128), (1, 64, 130, 1000, 17)]:
+        q = W.bf16_bits(rng.standard_normal((Nq, H, D)).astype(np.float32))
+        kc, kts = W.int8_cache(int(rng.integers(1 << 30)), 5, H, Nk, D)
+        vc, vts = W.int8_cache(int(rng.integers(1 << 30)), 6, H, Nk, D)
+        out, ws = qa.attention_i8kv(dev_bf16(q), torch.from_numpy(kc).cuda(), torch.from_numpy(kts).cuda(),
+                                    torch.from_numpy(vc).cuda(), torch.from_numpy(vts).cuda(), pos0,
+                                    out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        ref, it = oracle.fwd_i8kv(q, kc, kts, vc, vts, pos0)
+        wsh = host(ws)
+        nkp, nqp = oracle.npad(Nk), oracle.npad(Nq)
+        assert np.array_equal(wsh[: H * D * nkp].reshape(H, D, nkp), it["v8t"])
+        off = (H * D * nkp + 255) // 256 * 256
+        assert np.array_equal(wsh[off: off + H * D * 4].view(np.float32).reshape(H, D), it["v_scale"])
+        off += (H * D * 4 + 255) // 256 * 256
+        assert np.array_equal(wsh[off: off + H * nqp * D].view(np.int8).reshape(H, nqp, D), it["q8"])
+        assert_close(host(out), ref, f"i8kv H={H} Nq={Nq} Nk={Nk} pos0={pos0}")
+
+
+# ----------------------------------------------------------------------------------
+# full-size workloads, sampled outputs
+# ----------------------------------------------------------------------------------
+def _sample_rows(Nq, rng, nblk=3):
+    blocks = sorted(set([0, (Nq - 1) // 64] + list(rng.integers(0, (Nq + 63) // 64, nblk))))
+    rows = [r for b in blocks for r in range(b * 64, min(Nq, b * 64 + 64))]
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("name", ["dense_b1_h16_n4096_d128", "video_dit_b1_h24_n37810_d128"])
+def test_dense_workload_full_size(qa, name):
+    w = W.BY_NAME[name]
+    say(f"full-size {w.name}: generating inputs")
+    q, k, v = W.dense_inputs(w)
+    dq, dk, dv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    out, inter = qa.attention(dq, dk, dv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    say("  oracle quantizers")
+    q8, qs, k8, ks, mean = oracle.quant_qk(q, k)
+    v8t, vs = oracle.quant_v(v)
+    assert np.array_equal(host(inter["k_mean"]), mean)
+    assert np.array_equal(host(inter["q8"]), q8) and np.array_equal(host(inter["q_scale"]), qs)
+    assert np.array_equal(host(inter["k8"]), k8) and np.array_equal(host(inter["k_scale"]), ks)
+    assert np.array_equal(host(inter["v8t"]), v8t) and np.array_equal(host(inter["v_scale"]), vs)
+    rng = np.random.default_rng(9)
+    rows = _sample_rows(w.Nq, rng, nblk=2 if w.Nq > 10000 else 3)
+    heads = sorted(set([0, w.H - 1, int(rng.integers(w.H))]))
+    say(f"  oracle attention on {len(rows)} rows x {len(heads)} heads")
+    lam = oracle.default_lambda(w.D)
+    sel = (slice(None), heads)
+    ref = oracle.attn(q8[sel], qs[sel], k8[sel], ks[sel], v8t[sel], vs[sel], w.Nq, w.Nk, lam, rows=rows)
+    got = host(out)[:, rows][:, :, heads]
+    r = assert_close(got, ref, w.name)
+    say(f"  max err / rms = {r:.2e}")
+    out16, _ = qa.attention(dq, dk, dv, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out16)[:, rows][:, :, heads], bf16_of(host(out)[:, rows][:, :, heads]))
+
+
+@pytest.mark.parametrize("name", ["prefill_i8kv_h32_d128_q1024_ctx32768", "prefill_i8kv_h32_d128_q512_ctx65536"])
+def test_i8kv_workload_full_size(qa, name):
+    w = W.BY_NAME[name]
+    say(f"full-size {w.name}: generating inputs")
+    q, kc, kts, vc, vts = W.i8kv_inputs(w)
+    out, ws = qa.attention_i8kv(dev_bf16(q), torch.from_numpy(kc).cuda(), torch.from_numpy(kts).cuda(),
+                                torch.from_numpy(vc).cuda(), torch.from_numpy(vts).cuda(), w.pos0,
+                                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    say("  oracle requant + quant")
+    v8t, vsc = oracle.requant_v_cache(vc, vts)
+    q8, qs = oracle.quant_i8_blocks(q[None])
+    wsh = host(ws)
+    H, D, nkp = w.H, w.D, oracle.npad(w.Nk)
+    assert np.array_equal(wsh[: H * D * nkp].reshape(H, D, nkp), v8t)
+    rng = np.random.default_rng(11)
+    rows = _sample_rows(w.Nq, rng, nblk=2)
+    heads = sorted(set([0, w.H - 1, int(rng.integers(w.H))]))
+    say(f"  oracle attention on {len(rows)} rows x {len(heads)} heads")
+    lam = oracle.default_lambda(D)
+    ref = oracle.attn(q8[:, heads], qs[:, heads], kc[None, heads], kts[None, heads], v8t[None, heads],
+                      vsc[None, heads], w.Nq, w.Nk, lam, causal=True, pos_off=w.pos0, k_scale_per_token=True,
+                      rows=rows)
+    got = host(out)[rows][:, heads][None]
+    r = assert_close(got, ref, w.name)
+    say(f"  max err / rms = {r:.2e}")
