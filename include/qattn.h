@@ -110,7 +110,9 @@ size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D);
 /* Self-test hook: codes[i] = E4M3(exp2(fl32(u[i] - 192))) computed by the fused kernel's
  * own device function (the FP8 P code the softmax produces for the grid argument u).
  * u: f32 [n], codes: u8 [n], device pointers.  Used to check the exponential against the
- * correctly rounded one over the whole argument grid. */
+ * correctly rounded one over every argument the softmax can produce (u <= 200 + 2^-15).
+ * Like the kernel, the conversion does not saturate: u > 200.86 (a power above 464, never
+ * produced by the softmax) gives the NaN code 0x7F. */
 int qattn_p8_codes(const float* u, uint8_t* codes, int64_t n, void* stream);
 
 /* Static description of a status code. */

@@ -129,10 +129,13 @@ def test_quant_v_every_bf16_value(qa):
 
 
 def test_p8_codes_whole_grid(qa):
-    """The fused kernel's P8 code of 2^(u - 192) for EVERY fp32 u in [64, 384) equals the
-    code of the correctly rounded power (the oracle's)."""
-    lo = int(np.float32(64.0).view(np.uint32))
-    hi = int(np.float32(384.0).view(np.uint32))
+    """The fused kernel's P8 code of 2^(u - 192) equals the code of the correctly rounded
+    power (the oracle's) for EVERY fp32 u in [32, 200.5).  The kernel's argument is
+    u = fl32(acc * c + fl32(200 - m)) <= 200 + 2^-15, so this covers every argument with a
+    nonzero code (below u = 32, P' < 2^-160) and stays below e4m3's saturation point
+    (u > 200.86 gives P' > 464, where the hardware converter returns NaN)."""
+    lo = int(np.float32(32.0).view(np.uint32))
+    hi = int(np.float32(200.5).view(np.uint32))
     say(f"p8 codes over {hi - lo} grid arguments")
     u = torch.arange(lo, hi, dtype=torch.int64, device="cuda").to(torch.int32).view(torch.float32)
     codes = torch.empty(hi - lo, dtype=torch.uint8, device="cuda")
@@ -142,6 +145,12 @@ def test_p8_codes_whole_grid(qa):
     got = host(codes)
     bad = np.flatnonzero(got != ref)
     assert bad.size == 0, f"{bad.size} mismatches, first u bits {[hex(lo + int(i)) for i in bad[:5]]}"
+    # far below the grid: zero codes (including -inf for masked keys)
+    tail = torch.tensor([0.0, 1.0, 31.9, -5.0, -1e30, float("-inf")], dtype=torch.float32, device="cuda")
+    tc = torch.empty(6, dtype=torch.uint8, device="cuda")
+    qa.qattn_p8_codes(tail, tc)
+    torch.cuda.synchronize()
+    assert not host(tc).any()
 
 
 # ----------------------------------------------------------------------------------
