@@ -50,13 +50,88 @@ __device__ __forceinline__ int key_of_row(int kb, int m) {
   return 32 * ((m >> 2) & 1) + 16 * kb + 4 * (m >> 3) + (m & 3);
 }
 
-// 16-byte-slot swizzles of the LDS tiles (row pitch D bytes for K, 64 bytes for V^T).
+// 16-byte-slot XOR swizzles of the LDS tiles (row pitch D bytes for K, 64 bytes for V^T).
+// Chosen so that the QK reads (lanes of a half wave read 32 key rows through
+// key_of_row at one chunk column) and the PV reads (32 consecutive channel rows) hit
+// distinct banks both when 8 lanes share a 128-byte bank cycle and when 16 lanes share
+// a 256-byte one.
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
-  if (D == 128) return (row & 3) | (((row >> 5) & 1) << 2);
-  return ((row >> 1) & 1) | (((row >> 5) & 1) << 1);
+  if (D == 128) return ((row ^ (row >> 2)) & 1) | (row & 2) | (((row >> 5) & 1) << 2);
+  return (((row >> 1) ^ (row >> 2)) & 1) | (((row >> 5) & 1) << 1);
 }
-__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int vswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// INT32 accumulators start at the bit pattern of 1.5 * 2^23, so that reading an
+// accumulator as fp32 and subtracting 1.5 * 2^23 gives the exact dot product
+// (|acc| <= 127 * 127 * 128 < 2^22) with one fast fp32 subtraction.
+[[maybe_unused]] constexpr int kAccBias = 0x4B400000;
+constexpr float kAccBiasF = 12582912.0f;
+__device__ __forceinline__ float acc_f32(int biased) { return __builtin_bit_cast(float, biased) - kAccBiasF; }
+
+// Online-softmax update of one 64-key tile for this lane's query and its 32 keys
+// (key0 + i, i = 16 kb + j held in S_kb[j]).  Returns the 32 FP8 codes of P' = 256 P
+// packed as the B operand of the PV MFMA; updates m, the lane's share of d', and alpha.
+template <bool MASKED, bool PER_TOKEN>
+__device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, const float* cp, float c_tile,
+                                            int key0, int vis_last, float& m, float& dsum, float& alpha) {
+  float cvec[32];
+  if (PER_TOKEN) {
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      const float4 c4 = *(const float4*)(cp + i);
+      cvec[i] = c4.x;
+      cvec[i + 1] = c4.y;
+      cvec[i + 2] = c4.z;
+      cvec[i + 3] = c4.w;
+    }
+  }
+  auto acc_of = [&](int i) { return i < 16 ? S0[i] : S1[i - 16]; };
+  auto vis = [&](int i) { return !MASKED || key0 + i <= vis_last; };
+  float Mt;
+  if (PER_TOKEN) {
+    Mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float sv = acc_f32(acc_of(i)) * cvec[i];
+      Mt = vis(i) ? fmaxf(Mt, sv) : Mt;
+    }
+    Mt = fmaxf(Mt, __shfl_xor(Mt, 32, 64));
+  } else {
+    int mx = INT_MIN;
+    if (!MASKED) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = max(mx, max(S0[i], S1[i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) mx = vis(i) ? max(mx, acc_of(i)) : mx;
+    }
+    mx = max(mx, __shfl_xor(mx, 32, 64));
+    Mt = mx == INT_MIN ? -INFINITY : acc_f32(mx) * c_tile;
+  }
+  const float mnew = fmaxf(m, Mt);
+  const float ms = mnew == -INFINITY ? 0.0f : mnew;
+  alpha = mnew == m ? 1.0f : __builtin_amdgcn_exp2f(m - ms);
+  const float bconst = 200.0f - ms;
+  m = mnew;
+  float ds = 0.0f;
+  v8i pf;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * w + e;
+      float pv = p_from_u(__builtin_fmaf(acc_f32(acc_of(i)), PER_TOKEN ? cvec[i] : c_tile, bconst));
+      if (MASKED) pv = vis(i) ? pv : 0.0f;
+      ds += pv;
+      p[e] = pv;
+    }
+    pf[w] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+  }
+  dsum = dsum * alpha + ds;
+  return pf;
+}
 
 template <int D, bool PER_TOKEN, bool CAUSAL>
 __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
@@ -185,8 +260,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
     v16i S0, S1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      S0[r] = 0;
-      S1[r] = 0;
+      S0[r] = kAccBias;
+      S1[r] = kAccBias;
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -198,77 +273,25 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
     }
 
     // ---- online softmax over this lane's 32 keys (key 32 hh + i, i = 16 kb + j) ----
-    const int64_t key0 = (int64_t)t * BN + 32 * hh;
-    const bool masked = ((int64_t)t * BN + BN > a.Nk) || (CAUSAL && (int64_t)t * BN + BN - 1 > (int64_t)qw + a.pos_off);
-    const int64_t vis_last = CAUSAL ? min((int64_t)qrow + a.pos_off, (int64_t)a.Nk - 1) : (int64_t)a.Nk - 1;
-    float cvec[32];
-    float c_tile = 0.0f;
-    float Mt;
-    if (PER_TOKEN) {
-      const float* cp = &sC[t & 1][wave >> 1][32 * hh];
-#pragma unroll
-      for (int i = 0; i < 32; i += 4) {
-        const float4 c4 = *(const float4*)(cp + i);
-        cvec[i] = c4.x;
-        cvec[i + 1] = c4.y;
-        cvec[i + 2] = c4.z;
-        cvec[i + 3] = c4.w;
-      }
-      Mt = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int acc = i < 16 ? S0[i] : S1[i - 16];
-        const float sv = (float)acc * cvec[i];
-        const bool vis = !masked || (key0 + i <= vis_last);
-        Mt = vis ? fmaxf(Mt, sv) : Mt;
-      }
-      Mt = fmaxf(Mt, __shfl_xor(Mt, 32, 64));
-    } else {
-      c_tile = (sq_w * a.k_scale[bh * a.ks_bh + t]) * a.lambda;
-      int mx = INT_MIN;
-      if (!masked) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = max(mx, max(S0[i], S1[i]));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int acc = i < 16 ? S0[i] : S1[i - 16];
-          mx = (key0 + i <= vis_last) ? max(mx, acc) : mx;
-        }
-      }
-      mx = max(mx, __shfl_xor(mx, 32, 64));
-      Mt = mx == INT_MIN ? -INFINITY : (float)mx * c_tile;
-    }
-    const float mnew = fmaxf(m, Mt);
-    const float ms = mnew == -INFINITY ? 0.0f : mnew;
-    const bool same = mnew == m;
-    const float alpha = same ? 1.0f : __builtin_amdgcn_exp2f(m - ms);
-    const float bconst = 200.0f - ms;
-    dsum *= alpha;
-
+    const int key0 = t * BN + 32 * hh;
+    const bool masked = (t * BN + BN > a.Nk) || (CAUSAL && (int64_t)t * BN + BN - 1 > (int64_t)qw + a.pos_off);
+    const float c_tile = PER_TOKEN ? 0.0f : (sq_w * a.k_scale[bh * a.ks_bh + t]) * a.lambda;
+    const float* cp = &sC[t & 1][wave >> 1][32 * hh];
+    float alpha;
     v8i pf;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * w + e;
-        const int acc = i < 16 ? S0[i] : S1[i - 16];
-        const float cc = PER_TOKEN ? cvec[i] : c_tile;
-        float pv = p_from_u(__builtin_fmaf((float)acc, cc, bconst));
-        if (masked) pv = (key0 + i <= vis_last) ? pv : 0.0f;
-        dsum += pv;
-        p[e] = pv;
-      }
-      pf[w] = pack_fp8x4(p[0], p[1], p[2], p[3]);
+    const float m_old = m;
+    if (masked) {
+      const int vis_last = (int)min(CAUSAL ? (int64_t)qrow + a.pos_off : (int64_t)a.Nk - 1, (int64_t)a.Nk - 1);
+      pf = softmax_tile<true, PER_TOKEN>(S0, S1, cp, c_tile, key0, vis_last, m, dsum, alpha);
+    } else {
+      pf = softmax_tile<false, PER_TOKEN>(S0, S1, cp, c_tile, key0, 0, m, dsum, alpha);
     }
-    if (__ballot(!same) != 0) {
+    if (__ballot(m != m_old) != 0) {
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[s][r] *= alpha;
     }
-    m = mnew;
 
     // ---- PV: O^T[32 channels x 32 queries] += V^T[channels x 64 keys] . P^T ----
 #pragma unroll
