@@ -44,6 +44,28 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
+// Direct global -> LDS load of 16 bytes per lane: lane l of the wave writes LDS bytes
+// [lds + 16 l, lds + 16 l + 16).  Issued as inline assembly so that the compiler does
+// not order the kernel's LDS reads after it (it would have to assume that the
+// asynchronous LDS write may alias them); completion is awaited explicitly with
+// s_waitcnt vmcnt(0) and a barrier before the buffer is read.  M0 (the LDS base) is
+// saved and restored around the load.
+__device__ __forceinline__ void dma_16B(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voffset, int soffset) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voffset), "s"(rsrc), "s"(soffset)
+      : "memory");
+}
+// wave-uniform LDS byte address of a shared-memory location
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p);
+}
+
 // Physical key (within the tile) of A-operand row m of the QK MFMA for 32-key block kb:
 // the accumulator row m lands in lane half (m >> 2) & 1, register 4 (m >> 3) + (m & 3).
 __device__ __forceinline__ int key_of_row(int kb, int m) {
@@ -61,6 +83,37 @@ __device__ __forceinline__ int kswz(int row) {
   return (((row >> 1) ^ (row >> 2)) & 1) | (((row >> 5) & 1) << 1);
 }
 __device__ __forceinline__ int vswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// Combine a value with the one held by the lane 32 apart (same query, other key half).
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with the lower 32
+// lanes of its second; applied to a value and a copy of it, every lane ends up holding
+// {own, partner} in its two registers (in some order), which max and sum combine.  It is
+// issued as assembly because the compiler folds the two results of the builtin into one
+// when both operands are the same value.  s_nop 1 covers the VALU-write -> permlane-read
+// hazard.
+__device__ __forceinline__ void own_and_partner(uint32_t x, uint32_t& a, uint32_t& b) {
+  a = x;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1"
+      : "+v"(a), "=&v"(b));
+}
+__device__ __forceinline__ int max_with_partner(int x) {
+  uint32_t a, b;
+  own_and_partner((uint32_t)x, a, b);
+  return max((int)a, (int)b);
+}
+__device__ __forceinline__ float fmax_with_partner(float x) {
+  uint32_t a, b;
+  own_and_partner(__builtin_bit_cast(uint32_t, x), a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float sum_with_partner(float x) {
+  uint32_t a, b;
+  own_and_partner(__builtin_bit_cast(uint32_t, x), a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
 
 // INT32 accumulators start at the bit pattern of 1.5 * 2^23, so that reading an
 // accumulator as fp32 and subtracting 1.5 * 2^23 gives the exact dot product
@@ -96,7 +149,7 @@ __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, cons
       const float sv = acc_f32(acc_of(i)) * cvec[i];
       Mt = vis(i) ? fmaxf(Mt, sv) : Mt;
     }
-    Mt = fmaxf(Mt, __shfl_xor(Mt, 32, 64));
+    Mt = fmax_with_partner(Mt);
   } else {
     int mx = INT_MIN;
     if (!MASKED) {
@@ -106,7 +159,7 @@ __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, cons
 #pragma unroll
       for (int i = 0; i < 32; ++i) mx = vis(i) ? max(mx, acc_of(i)) : mx;
     }
-    mx = max(mx, __shfl_xor(mx, 32, 64));
+    mx = max_with_partner(mx);
     Mt = mx == INT_MIN ? -INFINITY : acc_f32(mx) * c_tile;
   }
   const float mnew = fmaxf(m, Mt);
@@ -206,15 +259,13 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
     const int vrow = slot >> 2, vpc = slot & 3;
     voff[i] = vrow * (int)a.ldv + 16 * (vpc ^ vswz(vrow));
   }
-  auto stage = [&](int t) {
+  auto stage = [&](int t) {  // DMA tile t into buffer t & 1
     const int buf = t & 1;
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int seg = wave * PT + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(&sK[buf][1024 * seg]),
-                                               16, koff[i], t * BN * D, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(&sV[buf][1024 * seg]),
-                                               16, voff[i], t * BN, 0, 0);
+      dma_16B(krs, lds_addr(&sK[buf][1024 * seg]), koff[i], t * BN * D);
+      dma_16B(vrs, lds_addr(&sV[buf][1024 * seg]), voff[i], t * BN);
     }
   };
   float cr = 0.0f;
@@ -246,12 +297,14 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
   __syncthreads();
 
   const int krow0 = key_of_row(0, l32), krow1 = key_of_row(1, l32);
+  const __attribute__((address_space(4))) float* ks_const =
+      (const __attribute__((address_space(4))) float*)uniform_ptr(a.k_scale + bh * a.ks_bh);
   for (int t = 0; t < ntiles; ++t) {
     const bool nxt = t + 1 < ntiles;
     // buffer (t+1)&1 was last read in iteration t-1, which ended with a barrier
     if (nxt) {
+      scale_load(t + 1);  // before the DMA, so waiting for it leaves the DMA in flight
       stage(t + 1);
-      scale_load(t + 1);
     }
     const uint8_t* tK = sK[t & 1];
     const uint8_t* tV = sV[t & 1];
@@ -275,7 +328,9 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
     // ---- online softmax over this lane's 32 keys (key 32 hh + i, i = 16 kb + j) ----
     const int key0 = t * BN + 32 * hh;
     const bool masked = (t * BN + BN > a.Nk) || (CAUSAL && (int64_t)t * BN + BN - 1 > (int64_t)qw + a.pos_off);
-    const float c_tile = PER_TOKEN ? 0.0f : (sq_w * a.k_scale[bh * a.ks_bh + t]) * a.lambda;
+    // per-tile K scale: uniform address, read through the constant address space so it
+    // is a scalar load (counted by lgkmcnt, not by the vmcnt of the in-flight K/V DMA)
+    const float c_tile = PER_TOKEN ? 0.0f : (sq_w * ks_const[t]) * a.lambda;
     const float* cp = &sC[t & 1][wave >> 1][32 * hh];
     float alpha;
     v8i pf;
@@ -310,7 +365,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
   }
 
   // ---- epilogue: out = O * s_v / d' ----
-  const float dt = dsum + __shfl_xor(dsum, 32, 64);
+  const float dt = sum_with_partner(dsum);
   if (qrow < a.Nq) {
     const int b = bh / a.H, h = bh - b * a.H;
     const int64_t off = b * a.out_sb + (int64_t)qrow * a.out_sn + h * a.out_sh;
