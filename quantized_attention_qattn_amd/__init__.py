@@ -81,6 +81,17 @@ def _need(t: torch.Tensor, dtype, name: str):
         raise TypeError(f"{name}: expected a {dtype} CUDA tensor")
 
 
+def _buf(t: torch.Tensor, dtype, shape, name: str):
+    """A code, scale or workspace buffer: the C ABI takes its base pointer and assumes the
+    dense layout, so its dtype, shape and contiguity are checked here."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dtype:
+        raise TypeError(f"{name}: expected a {dtype} CUDA tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
 def npad(n: int) -> int:
     return (n + BLOCK - 1) // BLOCK * BLOCK
 
@@ -95,6 +106,11 @@ def qattn_quant_qk(q, k, q8, q_scale, k8, k_scale, k_mean, stream=None) -> None:
     Nk = k.shape[1]
     if k.shape[0] != B or k.shape[2] != H or k.shape[3] != D:
         raise ValueError("q and k must agree on B, H, D")
+    _buf(q8, torch.int8, (B, H, npad(Nq), D), "q8")
+    _buf(q_scale, torch.float32, (B, H, npad(Nq) // BLOCK), "q_scale")
+    _buf(k8, torch.int8, (B, H, npad(Nk), D), "k8")
+    _buf(k_scale, torch.float32, (B, H, npad(Nk) // BLOCK), "k_scale")
+    _buf(k_mean, torch.float32, (B, H, D), "k_mean")
     _check(_lib.qattn_quant_qk(_ptr(q), _I64x3(*q.stride()[:3]), _ptr(k), _I64x3(*k.stride()[:3]), B, H, Nq, Nk, D,
                                _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(k_mean), _stream(stream)),
            "qattn_quant_qk")
@@ -103,6 +119,8 @@ def qattn_quant_qk(q, k, q8, q_scale, k8, k_scale, k_mean, stream=None) -> None:
 def qattn_quant_v(v, v8t, v_scale, stream=None) -> None:
     _need(v, torch.bfloat16, "v")
     B, Nk, H, D = v.shape
+    _buf(v8t, torch.uint8, (B, H, D, npad(Nk)), "v8t")
+    _buf(v_scale, torch.float32, (B, H, D), "v_scale")
     _check(_lib.qattn_quant_v(_ptr(v), _I64x3(*v.stride()[:3]), B, H, Nk, D, _ptr(v8t), _ptr(v_scale),
                               _stream(stream)), "qattn_quant_v")
 
@@ -110,6 +128,14 @@ def qattn_quant_v(v, v8t, v_scale, stream=None) -> None:
 def qattn_fwd(q8, q_scale, k8, k_scale, v8t, v_scale, Nq: int, Nk: int, out, scale_log2: float = 0.0,
               causal: bool = False, stream=None) -> None:
     B, H, _, D = q8.shape
+    _buf(q8, torch.int8, (B, H, npad(Nq), D), "q8")
+    _buf(q_scale, torch.float32, (B, H, npad(Nq) // BLOCK), "q_scale")
+    _buf(k8, torch.int8, (B, H, npad(Nk), D), "k8")
+    _buf(k_scale, torch.float32, (B, H, npad(Nk) // BLOCK), "k_scale")
+    _buf(v8t, torch.uint8, (B, H, D, npad(Nk)), "v8t")
+    _buf(v_scale, torch.float32, (B, H, D), "v_scale")
+    if not out.is_cuda or tuple(out.shape) != (B, Nq, H, D) or out.stride(3) != 1:
+        raise ValueError(f"out: expected a CUDA [B, Nq, H, D] = {(B, Nq, H, D)} view with unit channel stride")
     od = QATTN_OUT_BF16 if out.dtype == torch.bfloat16 else QATTN_OUT_F32 if out.dtype == torch.float32 else -1
     _check(_lib.qattn_fwd(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8t), _ptr(v_scale), B, H, Nq, Nk,
                           D, float(scale_log2), 1 if causal else 0, _ptr(out), _I64x3(*out.stride()[:3]), od,
@@ -125,6 +151,14 @@ def qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, wor
     _need(q, torch.bfloat16, "q")
     Nq, H, D = q.shape
     Nk = k_cache.shape[1]
+    _buf(k_cache, torch.int8, (H, Nk, D), "k_cache")
+    _buf(k_tok_scale, torch.float32, (H, Nk), "k_tok_scale")
+    _buf(v_cache, torch.int8, (H, Nk, D), "v_cache")
+    _buf(v_tok_scale, torch.float32, (H, Nk), "v_tok_scale")
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace: expected a contiguous CUDA tensor")
+    if not out.is_cuda or tuple(out.shape) != (Nq, H, D) or out.stride(2) != 1:
+        raise ValueError(f"out: expected a CUDA [Nq, H, D] = {(Nq, H, D)} view with unit channel stride")
     od = QATTN_OUT_BF16 if out.dtype == torch.bfloat16 else QATTN_OUT_F32 if out.dtype == torch.float32 else -1
     _check(_lib.qattn_fwd_i8kv(_ptr(q), _I64x2(*q.stride()[:2]), _ptr(k_cache), _ptr(k_tok_scale), _ptr(v_cache),
                                _ptr(v_tok_scale), H, Nq, Nk, D, int(pos0), float(scale_log2), _ptr(workspace),
@@ -134,6 +168,8 @@ def qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, wor
 
 def qattn_p8_codes(u, codes, stream=None) -> None:
     _need(u, torch.float32, "u")
+    _buf(u, torch.float32, (u.numel(),), "u")
+    _buf(codes, torch.uint8, (u.numel(),), "codes")
     _check(_lib.qattn_p8_codes(_ptr(u), _ptr(codes), u.numel(), _stream(stream)), "qattn_p8_codes")
 
 

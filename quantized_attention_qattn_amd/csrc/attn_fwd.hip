@@ -1,25 +1,43 @@
 // Fused quantized attention forward for gfx950: INT8 MFMA Q.K^T with INT32 accumulation,
-// tile-ordered online softmax with FP8 P, FP8 MFMA P.V, fused V-scale epilogue.
+// tile-ordered online softmax with FP8 P, P.V over the FP8 values of P and V, fused
+// V-scale epilogue.
 //
 // Per 64-key tile every query row runs QK -> update m, d, O -> accumulate d -> P to FP8
 // -> PV ("Sage2 SM89 Temporal Pair Experiment", section "Candidate"), so each row's
 // numeric sequence is independent of how rows are grouped into waves.
 //
 // Layout of the work (CDNA4, 64-wide waves):
-//   * a workgroup owns 128 query rows of one (b, h): 4 waves x 32 rows;
+//   * a workgroup owns 256 query rows of one (b, h): 8 waves x 32 rows.  Waves w and
+//     w + 4 share a SIMD.  Each wave alternates an MFMA phase (QK of tile i and PV of
+//     tile i - 1) with a VALU phase (online softmax of tile i); group 1 (waves 4-7) runs
+//     one phase behind group 0, so while one wave of a SIMD issues matrix instructions its
+//     partner is in the softmax.  (Measured on MI355X: a wave that interleaves both kinds
+//     of work in its own instruction stream overlaps them far less.)
 //   * scores are computed transposed, S^T = K . Q^T, with v_mfma_i32_32x32x32_i8: the
 //     accumulator gives each lane one query (its column) and 32 keys of the tile (16 per
 //     32-key block), so the row max and row sum are in-lane plus one exchange with the
 //     lane 32 apart;
-//   * the key order inside a tile is permuted so that lane half h holds keys 32h..32h+31:
-//     K rows are read from LDS through that permutation, so the lane's 32 FP8 P values
-//     are exactly the B operand of v_mfma_f32_32x32x64_f8f6f4 for those 32 keys, and the
-//     A operand (V^T) is a contiguous 32-byte run of the channel-major V tile;
+//   * the key order inside a tile is permuted so that lane half h holds keys 32h..32h+31;
+//     its 32 P values then form, 8 keys at a time, the B operand of four
+//     v_mfma_f32_32x32x16_bf16 whose A operand (V^T) is read from LDS at the same keys;
+//   * P.V runs on the bf16 MFMA over the exact values of the FP8 codes of P and V (every
+//     e4m3 value is a bf16 value, every product of two is exact in fp32).  The FP8 MFMA
+//     of gfx950 was not used here: it truncates each product to 13 bits below the
+//     largest product of its group of 8, which moves outputs by up to ~1e-3 of their
+//     RMS and breaks the accuracy contract;
 //   * O^T (D x 32 queries per wave) lives in D/32 accumulators of 16 fp32 per lane;
-//   * K and V^T tiles are staged in LDS (16-byte XOR swizzles against bank conflicts),
-//     the next tile is fetched into registers while the current one is consumed;
+//   * K tiles (INT8) and V^T tiles (FP8 codes) are loaded straight into LDS; each group
+//     widens half of every V^T tile to bf16 in its VALU phase;
 //   * workgroups are mapped so each XCD walks one contiguous range of (b, h, query block)
 //     and keeps the K/V it streams in its own L2.
+//
+// Tile pipeline (tick k = the interval between two workgroup barriers; group 0 runs
+// phase k of its sequence M0 V0 M1 V1 ..., group 1 phase k - 1):
+//   slot j = {K tile j, V^T codes of tile j} is loaded by group 0 at the start of its
+//   MFMA phase j - 1 (tick 2j - 2) and waited for at the end of its VALU phase j - 1
+//   (tick 2j - 1); the bf16 V^T of tile j is written by group 1 at tick 2j and by group 0
+//   at tick 2j + 1, and read by the MFMA phases j + 1 (ticks 2j + 2 and 2j + 3).  Every
+//   buffer is reused two ticks after its last reader, so double buffering suffices.
 #include <climits>
 
 #include "common.h"
@@ -27,13 +45,13 @@
 namespace qattn {
 namespace detail {
 
-constexpr int BM = 128;  // query rows per workgroup
+constexpr int BM = 256;  // query rows per workgroup
 [[maybe_unused]] constexpr int BN = 64;   // keys per tile (the numeric contract's tile)
-constexpr int NT = 256;  // threads per workgroup
-// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9
-// encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+constexpr int NT = 512;  // threads per workgroup (8 waves)
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt_hi[15:14]): vmcnt(0) with the others at their maxima, and lgkmcnt(0) likewise.
 [[maybe_unused]] constexpr int kVmcntZero = 0x0F70;
-
+[[maybe_unused]] constexpr int kLgkmcntZero = 0xC07F;
 // P' = 2^fl32(u - 192): the exponent argument on its fixed grid, evaluated with the
 // hardware exponential.  On this grid the e4m3 code of the result equals the code of
 // the correctly rounded power (checked over every fp32 u by qattn_p8_codes).
@@ -72,17 +90,19 @@ __device__ __forceinline__ int key_of_row(int kb, int m) {
   return 32 * ((m >> 2) & 1) + 16 * kb + 4 * (m >> 3) + (m & 3);
 }
 
-// 16-byte-slot XOR swizzles of the LDS tiles (row pitch D bytes for K, 64 bytes for V^T).
-// Chosen so that the QK reads (lanes of a half wave read 32 key rows through
-// key_of_row at one chunk column) and the PV reads (32 consecutive channel rows) hit
-// distinct banks both when 8 lanes share a 128-byte bank cycle and when 16 lanes share
-// a 256-byte one.
+// 16-byte-slot XOR swizzle of the K tile (row pitch D bytes), chosen so that the QK
+// reads (lanes of a half wave read 32 key rows through key_of_row at one chunk column)
+// hit distinct banks both when 8 lanes share a 128-byte bank cycle and when 16 lanes
+// share a 256-byte one.
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
   if (D == 128) return ((row ^ (row >> 2)) & 1) | (row & 2) | (((row >> 5) & 1) << 2);
   return (((row >> 1) ^ (row >> 2)) & 1) | (((row >> 5) & 1) << 1);
 }
-__device__ __forceinline__ int vswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// bf16 V^T rows are 128 bytes (64 keys); the 16-byte chunk q of row r sits at q ^ vbswz(r).
+// The PV reads (32 consecutive rows at one chunk) then hit distinct banks both when 8
+// lanes share a 128-byte bank cycle and when 16 lanes share a 256-byte one.
+__device__ __forceinline__ int vbswz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Combine a value with the one held by the lane 32 apart (same query, other key half).
 // v_permlane32_swap exchanges the upper 32 lanes of its first operand with the lower 32
@@ -186,20 +206,43 @@ __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, cons
   return pf;
 }
 
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Exact bf16 values of four packed e4m3 codes (bytes 0..3 -> elements 0..3 of two words).
+__device__ __forceinline__ void fp8x4_to_bf16(int codes, uint32_t& lo, uint32_t& hi) {
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true));
+}
+
+// Workgroup barrier that waits only for this wave's LDS and scalar-memory operations
+// (not for the in-flight tile loads, as the fence of __syncthreads would); the
+// scheduling barriers keep the compiler from moving work across a phase boundary.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int D, bool PER_TOKEN, bool CAUSAL>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   // The body uses device-only types (buffer resources); the host pass only needs the
   // kernel's launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NS = D / 32;   // QK k-steps = O accumulator blocks
-  constexpr int KCH = D / 16;  // 16-byte chunks per K row
-  constexpr int PT = D / 64;   // 16-byte chunks per thread per tile (K and V each)
-  // double-buffered tiles: buffer t & 1 holds tile t
-  __shared__ __align__(16) uint8_t sK[2][BN * D];
-  __shared__ __align__(16) uint8_t sV[2][D * BN];
-  __shared__ __align__(16) float sC[2][2][BN];  // PER_TOKEN: c_j per (buffer, query block, key)
+  constexpr int NS = D / 32;        // QK k-steps = O accumulator blocks
+  constexpr int KCH = D / 16;       // 16-byte chunks per K row
+  constexpr int PT = D / 64;        // 16-byte chunks per loading thread per tile (K and V each)
+  constexpr int QB = BM / kBlk;     // 64-row Q scale blocks per workgroup
+  constexpr int VSLOTS = D * BN / 16;  // 16-byte code chunks per V^T tile
+  __shared__ __align__(16) uint8_t sK[2][BN * D];        // K codes, swizzled for the QK reads
+  __shared__ __align__(16) uint8_t sVc[2][D * BN];       // V^T codes, linear (DMA target)
+  __shared__ __align__(16) uint8_t sVb[2][D * BN * 2];   // V^T bf16, swizzled for the PV reads
+  __shared__ __align__(16) float sC[2][QB][BN];          // PER_TOKEN: c_j per (buffer, query block, key)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2;  // group 0 loads the tiles and leads by one phase
+  const int gtid = tid & 255;  // thread index within the group
   const int l32 = lane & 31, hh = lane >> 5;
   const int nqb = (a.Nq + BM - 1) / BM;
   // wave-uniform by construction; readfirstlane lets the compiler keep it in SGPRs
@@ -224,26 +267,30 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
     for (int s = 0; s < NS; ++s) qf[s] = v4i{0, 0, 0, 0};
   }
   const float sq_w = wave_live ? a.q_scale[bh * a.qs_bh + qw / kBlk] : 0.0f;
-  float sq_blk[2] = {0.0f, 0.0f};
-  if (PER_TOKEN) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (q0 + kBlk * i < a.nq_pad) sq_blk[i] = a.q_scale[bh * a.qs_bh + q0 / kBlk + i];
-  }
+  // group 0 thread t computes c for query block t / 64 and key t % 64 of each tile
+  float sq_mine = 0.0f;
+  if (PER_TOKEN && grp == 0 && q0 + kBlk * (gtid >> 6) < a.nq_pad)
+    sq_mine = a.q_scale[bh * a.qs_bh + q0 / kBlk + (gtid >> 6)];
 
+  // tiles streamed by the workgroup, and tiles holding a key visible to this wave
   int ntiles = (a.Nk + BN - 1) / BN;
+  int wtiles = wave_live ? ntiles : 0;
   if (CAUSAL) {
     int64_t last = (int64_t)min(q0 + BM, a.Nq) - 1 + a.pos_off;
     if (last > a.Nk - 1) last = a.Nk - 1;
     ntiles = last < 0 ? 0 : (int)(last / BN) + 1;
+    int64_t wlast = (int64_t)min(qw + 32, a.Nq) - 1 + a.pos_off;
+    if (wlast > a.Nk - 1) wlast = a.Nk - 1;
+    wtiles = (!wave_live || wlast < 0) ? 0 : (int)(wlast / BN) + 1;
   }
+  wtiles = __builtin_amdgcn_readfirstlane(wtiles);
 
   // ---- staging: global -> LDS directly (buffer loads with the LDS destination) ----
-  // Each wave fills PT 1 KiB segments of the K tile and of the V^T tile; lane l of a
-  // segment writes LDS slot 64 seg + l (16 bytes), so each lane fetches the global chunk
-  // that the swizzled layout keeps in that slot.  Buffer resources are per (b, h) with
-  // 32-bit offsets; rows past the end of the resource (a KV cache whose length is not a
-  // multiple of 64) read as zeros.
+  // Each group-0 wave fills PT 1 KiB segments of the K tile and of the V^T code tile;
+  // lane l of a segment writes LDS slot 64 seg + l (16 bytes), so each lane fetches the
+  // global chunk that the layout keeps in that slot (K: swizzled; V^T codes: linear).
+  // Buffer resources are per (b, h) with 32-bit offsets; rows past the end of the
+  // resource (a KV cache whose length is not a multiple of 64) read as zeros.
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(a.k8 + bh * a.k8_bh), (short)0, a.k_rows * D, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -253,31 +300,44 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
   int koff[PT], voff[PT];
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
-    const int slot = 64 * (wave * PT + i) + lane;
+    const int slot = 64 * ((wave & 3) * PT + i) + lane;
     const int row = slot / KCH, pc = slot % KCH;
     koff[i] = row * D + 16 * (pc ^ kswz<D>(row));
-    const int vrow = slot >> 2, vpc = slot & 3;
-    voff[i] = vrow * (int)a.ldv + 16 * (vpc ^ vswz(vrow));
+    voff[i] = (slot >> 2) * (int)a.ldv + 16 * (slot & 3);
   }
-  auto stage = [&](int t) {  // DMA tile t into buffer t & 1
-    const int buf = t & 1;
+  auto stage = [&](int t) {  // K and V^T codes of tile t -> buffers t & 1
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      const int seg = wave * PT + i;
-      dma_16B(krs, lds_addr(&sK[buf][1024 * seg]), koff[i], t * BN * D);
-      dma_16B(vrs, lds_addr(&sV[buf][1024 * seg]), voff[i], t * BN);
+      const int seg = (wave & 3) * PT + i;
+      dma_16B(krs, lds_addr(&sK[t & 1][1024 * seg]), koff[i], t * BN * D);
+      dma_16B(vrs, lds_addr(&sVc[t & 1][1024 * seg]), voff[i], t * BN);
     }
   };
-  float cr = 0.0f;
+  // The raw key scale is multiplied only at store time, after the explicit wait for the
+  // tile loads: a use right after the load would make the compiler wait for the loads
+  // issued behind it.
+  float skr = 0.0f;
   auto scale_load = [&](int t) {
-    if (PER_TOKEN && tid < 2 * BN) {
-      const float sk =
-          __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 4 * (tid & (BN - 1)), 4 * t * BN, 0));
-      cr = (sq_blk[tid / BN] * sk) * a.lambda;
-    }
+    if (PER_TOKEN)
+      skr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 4 * (gtid & (BN - 1)), 4 * t * BN, 0));
   };
   auto scale_store = [&](int t) {
-    if (PER_TOKEN && tid < 2 * BN) sC[t & 1][tid / BN][tid & (BN - 1)] = cr;
+    if (PER_TOKEN) sC[t & 1][gtid >> 6][gtid & (BN - 1)] = (sq_mine * skr) * a.lambda;
+  };
+  // Widen this group's half of the V^T codes of tile t to bf16: one 16-code chunk
+  // (row r, keys 16 kc .. 16 kc + 15) per thread, written as bf16 chunks 2 kc, 2 kc + 1.
+  auto widen_v = [&](int t) {
+    const int slot = grp * (VSLOTS / 2) + gtid;
+    if (VSLOTS / 2 == 256 || gtid < VSLOTS / 2) {
+      const v4i c = *(const v4i*)&sVc[t & 1][16 * slot];
+      const int r = slot >> 2, kc = slot & 3;
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fp8x4_to_bf16(c[e], w[2 * e], w[2 * e + 1]);
+      uint8_t* rowp = &sVb[t & 1][r * (2 * BN)];
+      *(v4i*)(rowp + 16 * ((2 * kc) ^ vbswz(r))) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      *(v4i*)(rowp + 16 * ((2 * kc + 1) ^ vbswz(r))) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    }
   };
 
   float m = -INFINITY;  // running max (log2 domain)
@@ -287,82 +347,106 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(FwdArgs a) {
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[s][r] = 0.0f;
+  v16i S0, S1;
+  uint32_t pb[16];  // bf16 P of the last softmax: keys 32 hh + 2 j, 2 j + 1 in word j
+#pragma unroll
+  for (int j = 0; j < 16; ++j) pb[j] = 0u;
 
-  if (ntiles > 0) {
-    stage(0);
+  if (grp == 0 && ntiles > 0) {
     scale_load(0);
+    stage(0);
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);
     scale_store(0);
   }
+  // Q fragment and scales are in registers before the loop: otherwise the compiler's
+  // waits for them, placed inside the loop, would also wait for the tile loads in flight
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
-  __syncthreads();
+  phase_barrier();
 
   const int krow0 = key_of_row(0, l32), krow1 = key_of_row(1, l32);
   const __attribute__((address_space(4))) float* ks_const =
       (const __attribute__((address_space(4))) float*)uniform_ptr(a.k_scale + bh * a.ks_bh);
-  for (int t = 0; t < ntiles; ++t) {
-    const bool nxt = t + 1 < ntiles;
-    // buffer (t+1)&1 was last read in iteration t-1, which ended with a barrier
-    if (nxt) {
-      scale_load(t + 1);  // before the DMA, so waiting for it leaves the DMA in flight
-      stage(t + 1);
-    }
-    const uint8_t* tK = sK[t & 1];
-    const uint8_t* tV = sV[t & 1];
-
-    // ---- QK: S^T for keys of block 0 and block 1 ----
-    v16i S0, S1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      S0[r] = kAccBias;
-      S1[r] = kAccBias;
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int ch = NS * hh + s;
-      const v4i k0 = *(const v4i*)(tK + krow0 * D + 16 * (ch ^ kswz<D>(krow0)));
-      S0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qf[s], S0, 0, 0, 0);
-      const v4i k1 = *(const v4i*)(tK + krow1 * D + 16 * (ch ^ kswz<D>(krow1)));
-      S1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qf[s], S1, 0, 0, 0);
-    }
-
-    // ---- online softmax over this lane's 32 keys (key 32 hh + i, i = 16 kb + j) ----
-    const int key0 = t * BN + 32 * hh;
-    const bool masked = (t * BN + BN > a.Nk) || (CAUSAL && (int64_t)t * BN + BN - 1 > (int64_t)qw + a.pos_off);
-    // per-tile K scale: uniform address, read through the constant address space so it
-    // is a scalar load (counted by lgkmcnt, not by the vmcnt of the in-flight K/V DMA)
-    const float c_tile = PER_TOKEN ? 0.0f : (sq_w * ks_const[t]) * a.lambda;
-    const float* cp = &sC[t & 1][wave >> 1][32 * hh];
-    float alpha;
-    v8i pf;
-    const float m_old = m;
-    if (masked) {
-      const int vis_last = (int)min(CAUSAL ? (int64_t)qrow + a.pos_off : (int64_t)a.Nk - 1, (int64_t)a.Nk - 1);
-      pf = softmax_tile<true, PER_TOKEN>(S0, S1, cp, c_tile, key0, vis_last, m, dsum, alpha);
-    } else {
-      pf = softmax_tile<false, PER_TOKEN>(S0, S1, cp, c_tile, key0, 0, m, dsum, alpha);
-    }
-    if (__ballot(m != m_old) != 0) {
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[s][r] *= alpha;
-    }
-
-    // ---- PV: O^T[32 channels x 32 queries] += V^T[channels x 64 keys] . P^T ----
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int vrow = 32 * s + l32;
-      const v4i va = *(const v4i*)(tV + vrow * BN + 16 * ((2 * hh) ^ vswz(vrow)));
-      const v4i vb = *(const v4i*)(tV + vrow * BN + 16 * ((2 * hh + 1) ^ vswz(vrow)));
-      const v8i vf = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-      O[s] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, O[s], 0, 0, 0, 127, 0, 127);
-    }
-
-    if (nxt) scale_store(t + 1);
-    // own LDS-bound loads of tile t+1 complete, then everyone's (and tile t is consumed)
-    __builtin_amdgcn_s_waitcnt(kVmcntZero);
-    __syncthreads();
+  if (grp == 1) {  // group 1's first tick: its half of the bf16 V^T of tile 0
+    if (ntiles > 0) widen_v(0);
+    phase_barrier();
   }
+  for (int i = 0; i <= ntiles; ++i) {
+    // ---- MFMA phase i: S = K_i . Q^T and O^T += V_{i-1}^T . P_{i-1}^T ----
+    if (grp == 0 && i + 1 < ntiles) {
+      scale_load(i + 1);
+      stage(i + 1);
+    }
+    if (i < wtiles) {
+      const uint8_t* tK = sK[i & 1];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        S0[r] = kAccBias;
+        S1[r] = kAccBias;
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int ch = NS * hh + s;
+        const v4i k0 = *(const v4i*)(tK + krow0 * D + 16 * (ch ^ kswz<D>(krow0)));
+        S0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k0, qf[s], S0, 0, 0, 0);
+        const v4i k1 = *(const v4i*)(tK + krow1 * D + 16 * (ch ^ kswz<D>(krow1)));
+        S1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(k1, qf[s], S1, 0, 0, 0);
+      }
+    }
+    if (i > 0 && i - 1 < wtiles) {
+      const uint8_t* tV = sVb[(i - 1) & 1];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const v8bf pfrag = __builtin_bit_cast(v8bf, v4i{(int)pb[4 * c], (int)pb[4 * c + 1], (int)pb[4 * c + 2],
+                                                        (int)pb[4 * c + 3]});
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int vrow = 32 * s + l32;
+          const v8bf vfrag = *(const v8bf*)(tV + vrow * (2 * BN) + 16 * ((4 * hh + c) ^ vbswz(vrow)));
+          O[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag, pfrag, O[s], 0, 0, 0);
+        }
+      }
+    }
+    phase_barrier();
+
+    // ---- VALU phase i: online softmax of tile i, and widening of V^T codes ----
+    if (i < wtiles) {
+      const int key0 = i * BN + 32 * hh;
+      const bool masked =
+          (i * BN + BN > a.Nk) || (CAUSAL && (int64_t)i * BN + BN - 1 > (int64_t)qw + a.pos_off);
+      // per-tile K scale: uniform address, read through the constant address space so it
+      // is a scalar load (counted by lgkmcnt, not by the vmcnt of the in-flight loads)
+      const float c_tile = PER_TOKEN ? 0.0f : (sq_w * ks_const[i]) * a.lambda;
+      const float* cp = &sC[i & 1][wave >> 1][32 * hh];
+      float alpha;
+      v8i pf;
+      const float m_old = m;
+      if (masked) {
+        const int vis_last = (int)min(CAUSAL ? (int64_t)qrow + a.pos_off : (int64_t)a.Nk - 1, (int64_t)a.Nk - 1);
+        pf = softmax_tile<true, PER_TOKEN>(S0, S1, cp, c_tile, key0, vis_last, m, dsum, alpha);
+      } else {
+        pf = softmax_tile<false, PER_TOKEN>(S0, S1, cp, c_tile, key0, 0, m, dsum, alpha);
+      }
+      if (__ballot(m != m_old) != 0) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) O[s][r] *= alpha;
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) fp8x4_to_bf16(pf[w], pb[2 * w], pb[2 * w + 1]);
+    }
+    if (grp == 0) {
+      if (i < ntiles) widen_v(i);
+      if (i + 1 < ntiles) {
+        __builtin_amdgcn_s_waitcnt(kVmcntZero);  // slot i + 1 (and its K scales) landed
+        scale_store(i + 1);
+      }
+    } else if (i + 1 < ntiles) {
+      widen_v(i + 1);
+    }
+    phase_barrier();
+  }
+  if (grp == 0) phase_barrier();
 
   // ---- epilogue: out = O * s_v / d' ----
   const float dt = sum_with_partner(dsum);
@@ -402,8 +486,7 @@ __global__ void p8_codes_kernel(const float* u, uint8_t* codes, int64_t n) {
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
-  const int nqb = (a.Nq + BM - 1) / BM;
-  const int grid = a.B * a.H * nqb;
+  const int grid = a.B * a.H * ((a.Nq + BM - 1) / BM);
   if (a.per_token) {
     if (a.causal)
       attn_fwd_kernel<D, true, true><<<grid, NT, 0, st>>>(a);

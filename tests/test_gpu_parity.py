@@ -287,6 +287,98 @@ def test_i8kv_small(qa):
 
 
 # ----------------------------------------------------------------------------------
+# many heads (grids of several hundred 256-row workgroups, every XCD busy)
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_many_heads_exact(qa, D, causal):
+    """Exact-score operands over 256 heads: GPU == oracle within 2 ulp."""
+    rng = np.random.default_rng(3000 + D + causal)
+    H = 256
+    for Nk in [1, 64, 65, 200, 333]:
+        for Nq in [1, 129, 300]:
+            if causal and Nq > Nk:
+                continue
+            say(f"many heads exact Nq={Nq} Nk={Nk} D={D} causal={causal}")
+            ops = _exact_ops(rng, Nq, Nk, D, H=H)
+            got = run_fwd(qa, ops, Nq, Nk, 1.0, causal)
+            ref = oracle.attn(*ops, Nq, Nk, 1.0, causal=causal)
+            ulp = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+            assert ulp.max() <= 2, (Nq, Nk, D, causal, ulp.max())
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_many_heads_random(qa, D, causal):
+    rng = np.random.default_rng(4000 + D + causal)
+    B, H = 2, 128
+    for Nq, Nk in [(257, 129), (300, 555), (600, 64), (64, 700)]:
+        if causal and Nq > Nk:
+            Nq, Nk = Nk, Nq
+        say(f"many heads random B={B} H={H} Nq={Nq} Nk={Nk} D={D} causal={causal}")
+        q = W.bf16_bits(rng.standard_normal((B, Nq, H, D)).astype(np.float32))
+        k = W.bf16_bits(rng.standard_normal((B, Nk, H, D)).astype(np.float32) + 1)
+        v = W.bf16_bits(rng.standard_normal((B, Nk, H, D)).astype(np.float32))
+        out, _ = qa.attention(dev_bf16(q), dev_bf16(k), dev_bf16(v), causal=causal, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        ref, _ = oracle.fwd(q, k, v, causal=causal)
+        assert_close(host(out), ref, f"B={B} H={H} Nq={Nq} Nk={Nk}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_head_split_bit_identical(qa, causal):
+    """Rows are independent: one call over 256 heads and the same heads in calls of 16
+    (other grid sizes, other workgroup-to-XCD mapping) give bit-identical outputs."""
+    rng = np.random.default_rng(77 + causal)
+    H, Nq, Nk, D, step = 256, 700, 1500, 128, 16
+    say(f"head split H={H} Nq={Nq} Nk={Nk} causal={causal}")
+    q = dev_bf16(W.bf16_bits(rng.standard_normal((1, Nq, H, D)).astype(np.float32)))
+    k = dev_bf16(W.bf16_bits(rng.standard_normal((1, Nk, H, D)).astype(np.float32)))
+    v = dev_bf16(W.bf16_bits(rng.standard_normal((1, Nk, H, D)).astype(np.float32)))
+    t = qa.alloc_qk(1, H, Nq, Nk, D)
+    tv = qa.alloc_v(1, H, Nk, D)
+    qa.qattn_quant_qk(q, k, t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["k_mean"])
+    qa.qattn_quant_v(v, tv["v8t"], tv["v_scale"])
+    whole = torch.empty((1, Nq, H, D), dtype=torch.float32, device="cuda")
+    parts = torch.empty_like(whole)
+    qa.qattn_fwd(t["q8"], t["q_scale"], t["k8"], t["k_scale"], tv["v8t"], tv["v_scale"], Nq, Nk, whole, 0.0, causal)
+    for h in range(0, H, step):
+        sl = slice(h, h + step)
+        qa.qattn_fwd(t["q8"][:, sl], t["q_scale"][:, sl], t["k8"][:, sl], t["k_scale"][:, sl], tv["v8t"][:, sl],
+                     tv["v_scale"][:, sl], Nq, Nk, parts[:, :, sl], 0.0, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int32), parts.view(torch.int32))
+
+
+def test_binding_rejects_strided_code_buffers(qa):
+    """Code buffers are passed by base pointer: a head slice of a B = 2 buffer is not
+    dense and must be refused before any launch."""
+    t = qa.alloc_qk(2, 4, 64, 64, 64)
+    tv = qa.alloc_v(2, 4, 64, 64)
+    out = torch.empty((2, 64, 2, 64), dtype=torch.float32, device="cuda")
+    sl = slice(0, 2)
+    with pytest.raises(ValueError):
+        qa.qattn_fwd(t["q8"][:, sl], t["q_scale"][:, sl], t["k8"][:, sl], t["k_scale"][:, sl], tv["v8t"][:, sl],
+                     tv["v_scale"][:, sl], 64, 64, out)
+
+
+def test_i8kv_many_heads(qa):
+    say("i8kv over many heads")
+    rng = np.random.default_rng(61)
+    for H, D, Nq, Nk, pos0 in [(256, 128, 100, 700, 600), (256, 64, 300, 1000, 17), (128, 128, 513, 600, 87)]:
+        say(f"  H={H} D={D} Nq={Nq} Nk={Nk} pos0={pos0}")
+        q = W.bf16_bits(rng.standard_normal((Nq, H, D)).astype(np.float32))
+        kc, kts = W.int8_cache(int(rng.integers(1 << 30)), 5, H, Nk, D)
+        vc, vts = W.int8_cache(int(rng.integers(1 << 30)), 6, H, Nk, D)
+        out, _ = qa.attention_i8kv(dev_bf16(q), torch.from_numpy(kc).cuda(), torch.from_numpy(kts).cuda(),
+                                   torch.from_numpy(vc).cuda(), torch.from_numpy(vts).cuda(), pos0,
+                                   out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        ref, _ = oracle.fwd_i8kv(q, kc, kts, vc, vts, pos0)
+        assert_close(host(out), ref, f"i8kv H={H} Nq={Nq} Nk={Nk} pos0={pos0}")
+
+
+# ----------------------------------------------------------------------------------
 # full-size workloads, sampled outputs
 # ----------------------------------------------------------------------------------
 def _sample_rows(Nq, rng, nblk=3):
