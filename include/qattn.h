@@ -73,9 +73,11 @@ int qattn_quant_qk(const void* q, const int64_t q_str[3], const void* k, const i
 int qattn_quant_v(const void* v, const int64_t v_str[3], int B, int H, int Nk, int D, uint8_t* v8t,
                   float* v_scale, void* stream);
 
-/* Steps 3-5 -- fused INT8 QK, online softmax with FP8 P, FP8 PV and epilogue ("Sage2 SM89
+/* Steps 3-5 -- fused INT8 QK, online softmax with FP8 P, PV and epilogue ("Sage2 SM89
  * Temporal Pair Experiment", "Candidate": per 64-key tile QK -> update m, d, O ->
  * accumulate d -> P to 8 bit -> PV), on the outputs of steps 1-2 (same layouts).
+ * PV sums the exact products of the e4m3 values of P and V in fp32 (no truncation of
+ * small products).
  *   scale_log2: softmax scale times log2(e); <= 0 selects fl32(fl32(1/sqrt(D)) * log2e).
  *   causal: key j visible to query i iff j <= i + (Nk - Nq) (bottom-right aligned); a
  *           query with no visible key outputs zeros.

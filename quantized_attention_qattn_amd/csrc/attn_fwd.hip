@@ -25,9 +25,10 @@
 //     of gfx950 was not used here: it truncates each product to 13 bits below the
 //     largest product of its group of 8, which moves outputs by up to ~1e-3 of their
 //     RMS and breaks the accuracy contract;
-//   * K tiles (INT8) and V^T tiles (FP8 codes) are loaded straight into LDS; V^T stays
-//     in FP8 there (half the LDS read traffic of a bf16 copy, which is what bounds the
-//     MFMA phase) and is widened to bf16 in registers right before each PV MFMA;
+//   * K tiles (INT8) and V^T tiles (FP8 codes) are loaded straight into LDS; each group-0
+//     wave widens the V^T chunks its own loads brought in to bf16 once, at the end of
+//     its VALU phase (where it would otherwise wait for group 1), so the MFMA phases
+//     read bf16 V^T fragments directly;
 //   * O^T (D x 32 queries per wave) lives in D/32 accumulators of 16 fp32 per lane;
 //   * workgroups are mapped so each XCD walks one contiguous range of (b, h, query block)
 //     and keeps the K/V it streams in its own L2.
@@ -35,11 +36,11 @@
 // Tile pipeline (tick k = the interval between two workgroup barriers; group 0 runs
 // phase k of its sequence M0 V0 M1 V1 ..., group 1 phase k - 1):
 //   slot j = {K tile j, V^T codes of tile j - 1} sits in buffer j % 3.  Group 0 issues
-//   the loads of slot j at the start of its MFMA phase j - 2 (tick 2j - 4) and waits for
-//   them at the end of its VALU phase j - 1 (tick 2j - 1), so a load has four ticks to
-//   land (measured: with one tick of slack the loads' latency, not the arithmetic,
-//   set the pace).  The MFMA phases j read slot j at ticks 2j (group 0) and 2j + 1
-//   (group 1); its buffer is reloaded at tick 2j + 2.
+//   the loads of slot j at the start of its MFMA phase j - 2 (tick 2j - 4), waits for
+//   them at the end of its VALU phase j - 1 (tick 2j - 1) and there widens the V^T
+//   codes into the bf16 buffer (j - 1) & 1.  The MFMA phases j read slot j and that
+//   bf16 tile at ticks 2j (group 0) and 2j + 1 (group 1); the slot buffer is reloaded
+//   at tick 2j + 2 and the bf16 buffer rewritten at tick 2j + 3.
 #include <climits>
 #include <type_traits>
 
@@ -119,9 +120,10 @@ __device__ __forceinline__ int kswz(int row) {
   if (D == 128) return ((row ^ (row >> 2)) & 1) | (row & 2) | (((row >> 5) & 1) << 2);
   return (((row >> 1) ^ (row >> 2)) & 1) | (((row >> 5) & 1) << 1);
 }
-// V^T code rows are 64 bytes (64 keys); the 16-byte chunk q of row r sits at q ^ vswz(r),
-// so that the PV reads (32 consecutive channel rows at one chunk) hit distinct banks.
-__device__ __forceinline__ int vswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// bf16 V^T rows are 128 bytes (64 keys); the 16-byte chunk q of row r sits at q ^ vbswz(r).
+// The PV reads (32 consecutive rows at one chunk) then hit distinct banks both when 8
+// lanes share a 128-byte bank cycle and when 16 lanes share a 256-byte one.
+__device__ __forceinline__ int vbswz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Combine a value with the one held by the lane 32 apart (same query, other key half).
 // v_permlane32_swap exchanges the upper 32 lanes of its first operand with the lower 32
@@ -256,7 +258,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   constexpr int PT = D / 64;        // 16-byte chunks per loading thread per tile (K and V each)
   constexpr int QB = BM / kBlk;     // 64-row Q scale blocks per workgroup
   __shared__ __align__(16) uint8_t sK[NBUF][BN * D];   // K codes, swizzled for the QK reads
-  __shared__ __align__(16) uint8_t sV[NBUF][D * BN];   // V^T codes, swizzled for the PV reads
+  __shared__ __align__(16) uint8_t sV[NBUF][D * BN];   // V^T codes, linear (loaded and widened by group 0)
+  __shared__ __align__(16) uint8_t sVb[2][D * BN * 2];  // V^T bf16 of tile j in buffer j & 1, swizzled
   __shared__ __align__(16) float sC[2][QB][BN];     // PER_TOKEN: c_j per (buffer, query block, key)
   __shared__ __align__(16) float sKs[NBUF][BN];     // PER_TOKEN: raw K scales of each slot
 
@@ -323,8 +326,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     const int slot = 64 * ((wave & 3) * PT + i) + lane;
     const int row = slot / KCH, pc = slot % KCH;
     koff[i] = row * D + 16 * (pc ^ kswz<D>(row));
-    const int vrow = slot >> 2, vpc = slot & 3;
-    voff[i] = vrow * (int)a.ldv + 16 * (vpc ^ vswz(vrow));
+    voff[i] = (slot >> 2) * (int)a.ldv + 16 * (slot & 3);
   }
   // Slot t: K tile t and its raw per-token K scales (t < ntiles), and the V^T codes of
   // tile t - 1 (t >= 1), into buffer buf = t % NBUF.  Every group-0 wave loads all 64
@@ -352,6 +354,25 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(PT + (PER_TOKEN ? 1 : 0)));
   };
+  // Widen the V^T codes this wave loaded into buffer buf (tile v) to bf16: lane l of
+  // segment seg holds code chunk 64 seg + l = (channel row r, keys 16 kc .. 16 kc + 15),
+  // written as bf16 chunks 2 kc and 2 kc + 1 of row r.
+  auto widen_v = [&](int v, int buf) {
+    v4i c[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) c[i] = *(const v4i*)&sV[buf][16 * (64 * ((wave & 3) * PT + i) + lane)];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int slot = 64 * ((wave & 3) * PT + i) + lane;
+      const int r = slot >> 2, kc = slot & 3;
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fp8x4_to_bf16(c[i][e], w[2 * e], w[2 * e + 1]);
+      uint8_t* rowp = &sVb[v & 1][r * (2 * BN)];
+      *(v4i*)(rowp + 16 * ((2 * kc) ^ vbswz(r))) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      *(v4i*)(rowp + 16 * ((2 * kc + 1) ^ vbswz(r))) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    }
+  };
   auto scale_store = [&](int t, int buf) {  // c of slot t (buffer buf), after its wait
     if (PER_TOKEN) sC[t & 1][gtid >> 6][gtid & (BN - 1)] = (sq_mine * sKs[buf][gtid & (BN - 1)]) * a.lambda;
   };
@@ -367,9 +388,10 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) pb[j] = 0u;
 
-  // slot 0 carries no V^T tile; its buffer is read once with P = 0 and must hold finite
-  // values (uninitialized LDS may hold NaN codes)
-  if (16 * tid < D * BN) *(v4i*)&sV[0][16 * tid] = v4i{0, 0, 0, 0};
+  // the first MFMA phase reads bf16 buffer 1 with P = 0: it must hold finite values
+  // (uninitialized LDS may hold NaN patterns)
+  if (16 * tid < 2 * D * BN) *(v4i*)&sVb[1][16 * tid] = v4i{0, 0, 0, 0};
+  if (D * BN > 8 * NT) *(v4i*)&sVb[1][16 * (tid + NT)] = v4i{0, 0, 0, 0};
   // Q fragment and scales are in registers before any tile load: otherwise the
   // compiler's waits for them, placed inside the loop, would also wait for the tile
   // loads in flight
@@ -401,27 +423,21 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     // consumed (register budget).  The PV MFMAs run chunk-major, so consecutive MFMAs
     // accumulate into different O blocks.
     const uint8_t* tK = sK[buf];
-    const uint8_t* tV = sV[buf];
-    // lane (channel row, half hh) reads the codes of keys 32 hh .. 32 hh + 31 of its row
-    // as two 16-byte chunks; chunk cp holds the keys of PV steps 2 cp and 2 cp + 1
-    auto read_v = [&](int s, int cp) {
+    const uint8_t* tV = sVb[(i + 1) & 1];  // bf16 V^T of tile i - 1
+    // lane (channel row, half hh) reads the bf16 V^T of keys 32 hh + 8 c .. + 7 of its row
+    auto read_v = [&](int s, int c) {
       const int vrow = 32 * s + l32;
-      return *(const v4i*)(tV + vrow * BN + 16 * ((2 * hh + cp) ^ vswz(vrow)));
+      return *(const v8bf*)(tV + vrow * (2 * BN) + 16 * ((4 * hh + c) ^ vbswz(vrow)));
     };
-    auto pv_step = [&](int c, const v4i* vcodes) {
+    auto pv_step = [&](int c, const v8bf* vfrag) {
       const v8bf pfrag = __builtin_bit_cast(v8bf, v4i{(int)pb[4 * c], (int)pb[4 * c + 1], (int)pb[4 * c + 2],
                                                       (int)pb[4 * c + 3]});
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        uint32_t w[4];
-        fp8x4_to_bf16(vcodes[s][2 * (c & 1)], w[0], w[1]);
-        fp8x4_to_bf16(vcodes[s][2 * (c & 1) + 1], w[2], w[3]);
-        const v8bf vfrag = __builtin_bit_cast(v8bf, v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]});
-        O[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag, pfrag, O[s], 0, 0, 0);
-      }
+      for (int s = 0; s < NS; ++s) O[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag[s], pfrag, O[s], 0, 0, 0);
     };
     {
-      v4i kf[2 * NS], vc0[NS], vc1[NS];
+      v4i kf[2 * NS];
+      v8bf vf0[NS], vf1[NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int ch = NS * hh + s;
@@ -429,7 +445,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
         kf[2 * s + 1] = *(const v4i*)(tK + krow1 * D + 16 * (ch ^ kswz<D>(krow1)));
       }
 #pragma unroll
-      for (int s = 0; s < NS; ++s) vc0[s] = read_v(s, 0);
+      for (int s = 0; s < NS; ++s) vf0[s] = read_v(s, 0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         S0[r] = kAccBias;
@@ -445,11 +461,15 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x100, 3 * NS, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * NS, 0);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) vc1[s] = read_v(s, 1);
-      pv_step(0, vc0);
-      pv_step(1, vc0);
-      pv_step(2, vc1);
-      pv_step(3, vc1);
+      for (int s = 0; s < NS; ++s) vf1[s] = read_v(s, 1);
+      pv_step(0, vf0);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) vf0[s] = read_v(s, 2);
+      pv_step(1, vf1);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) vf1[s] = read_v(s, 3);
+      pv_step(2, vf0);
+      pv_step(3, vf1);
     }
     phase_barrier();
 
@@ -485,6 +505,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     }
     if (grp == 0 && i < ntiles) {
       wait_all_but(i + 2);  // slot i + 1 (and its K scales) landed
+      widen_v(i, buf1);     // V^T of tile i, read by the MFMA phases i + 1
       if (i + 1 < ntiles) scale_store(i + 1, buf1);
     }
     phase_barrier();
