@@ -334,13 +334,16 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   // wait makes them visible to it.  All slot traffic goes through the direct-to-LDS
   // loads: a compiler-visible load whose value is used while tile loads are in flight
   // would make the compiler wait for all of them.
+  // LDS byte addresses of the buffers, formed once (wave-uniform)
+  const uint32_t ldsK0 = lds_addr(&sK[0][0]), ldsV0 = lds_addr(&sV[0][0]), ldsKs0 = lds_addr(&sKs[0][0]);
   auto stage = [&](int t, int buf) {
-    if (PER_TOKEN && t < ntiles) dma_4B(srs, lds_addr(&sKs[buf][0]), 4 * lane, 4 * t * BN);
+    if (PER_TOKEN && t < ntiles) dma_4B(srs, ldsKs0 + buf * (4 * BN), 4 * lane, 4 * t * BN);
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
-      const int seg = (wave & 3) * PT + i;
-      if (t < ntiles) dma_16B(krs, lds_addr(&sK[buf][1024 * seg]), koff[i], t * BN * D);
-      if (t > 0) dma_16B(vrs, lds_addr(&sV[buf][1024 * seg]), voff[i], (t - 1) * BN);
+      // wave-uniform; readfirstlane tells the compiler so (the asm needs an SGPR)
+      const uint32_t seg = __builtin_amdgcn_readfirstlane(1024u * ((wave & 3) * PT + i));
+      if (t < ntiles) dma_16B(krs, ldsK0 + buf * (BN * D) + seg, koff[i], t * BN * D);
+      if (t > 0) dma_16B(vrs, ldsV0 + buf * (D * BN) + seg, voff[i], (t - 1) * BN);
     }
   };
   // wait until at most the loads of slot t are in flight (t > ntiles: none)
@@ -357,10 +360,12 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   // Widen the V^T codes this wave loaded into buffer buf (tile v) to bf16: lane l of
   // segment seg holds code chunk 64 seg + l = (channel row r, keys 16 kc .. 16 kc + 15),
   // written as bf16 chunks 2 kc and 2 kc + 1 of row r.
-  auto widen_v = [&](int v, int buf) {
-    v4i c[PT];
+  // (load at the start of the VALU phase, widen and store at its end)
+  auto widen_load = [&](int buf, v4i* c) {
 #pragma unroll
     for (int i = 0; i < PT; ++i) c[i] = *(const v4i*)&sV[buf][16 * (64 * ((wave & 3) * PT + i) + lane)];
+  };
+  auto widen_store = [&](int v, const v4i* c) {
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int slot = 64 * ((wave & 3) * PT + i) + lane;
@@ -407,6 +412,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   const int krow0 = key_of_row(0, l32), krow1 = key_of_row(1, l32);
   const __attribute__((address_space(4))) float* ks_const =
       (const __attribute__((address_space(4))) float*)uniform_ptr(a.k_scale + bh * a.ks_bh);
+  const int nkb = (a.Nk + BN - 1) / BN;  // K scale blocks
+  float ks_next = (!PER_TOKEN && ntiles > 0) ? ks_const[0] : 0.0f;
   if (grp == 1) phase_barrier();
   int buf = 0;  // buffer of slot i
   for (int i = 0; i <= ntiles; ++i) {
@@ -474,13 +481,23 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     phase_barrier();
 
     // ---- VALU phase i: online softmax of tile i ----
+    // group 0: slot i + 1 landed long ago (issued three ticks back); its V^T codes are
+    // read now and widened after the softmax, so the read latency is hidden
+    v4i wcodes[PT];
+    if (grp == 0 && i < ntiles) {
+      wait_all_but(i + 2);
+      widen_load(buf1, wcodes);
+    }
+    // per-tile K scale of this tile (loaded during the previous VALU phase) and of the
+    // next one: uniform addresses read through the constant address space, i.e. scalar
+    // loads, issued a phase ahead so that their latency is never waited for
+    const float ks_cur = ks_next;
+    if (!PER_TOKEN && i + 1 < nkb) ks_next = ks_const[i + 1];
     if (i < wtiles) {
       const int key0 = i * BN + 32 * hh;
       const bool masked =
           (i * BN + BN > a.Nk) || (CAUSAL && (int64_t)i * BN + BN - 1 > (int64_t)qw + a.pos_off);
-      // per-tile K scale: uniform address, read through the constant address space so it
-      // is a scalar load (counted by lgkmcnt, not by the vmcnt of the in-flight loads)
-      const float c_tile = PER_TOKEN ? 0.0f : (sq_w * ks_const[i]) * a.lambda;
+      const float c_tile = PER_TOKEN ? 0.0f : (sq_w * ks_cur) * a.lambda;
       const float* cp = &sC[i & 1][wave >> 1][32 * hh];
       float alpha;
       v8i pf;
@@ -504,8 +521,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
       for (int j = 0; j < 16; ++j) pb[j] = 0u;  // no contribution from this tile
     }
     if (grp == 0 && i < ntiles) {
-      wait_all_but(i + 2);  // slot i + 1 (and its K scales) landed
-      widen_v(i, buf1);     // V^T of tile i, read by the MFMA phases i + 1
+      widen_store(i, wcodes);  // V^T of tile i, read by the MFMA phases i + 1
       if (i + 1 < ntiles) scale_store(i + 1, buf1);
     }
     phase_barrier();
