@@ -109,11 +109,12 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
  * Returns 0 for invalid sizes. */
 size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D);
 
-/* Self-test hook: codes[i] = E4M3(exp2(fl32(u[i] - 192))) computed by the fused kernel's
- * own device function (the FP8 P code the softmax produces for the grid argument u).
+/* Self-test hook: codes[i] = E4M3(2^(u[i] - 80)) computed by the fused kernel's own
+ * device functions (the FP8 P code the softmax produces for the grid argument u: the
+ * hardware exponential of u, then the FP8 conversion with the exact 2^80 scale).
  * u: f32 [n], codes: u8 [n], device pointers.  Used to check the exponential against the
- * correctly rounded one over every argument the softmax can produce (u <= 200 + 2^-15).
- * Like the kernel, the conversion does not saturate: u > 200.86 (a power above 464, never
+ * correctly rounded one over every argument the softmax can produce (u <= 88 + 2^-16).
+ * Like the kernel, the conversion does not saturate: u > 88.86 (a power above 464, never
  * produced by the softmax) gives the NaN code 0x7F. */
 int qattn_p8_codes(const float* u, uint8_t* codes, int64_t n, void* stream);
 

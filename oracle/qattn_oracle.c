@@ -100,11 +100,15 @@ uint8_t orc_e4m3_encode(float x) {
 /* 2^x rounded to the nearest fp32.  Evaluated as (float)exp2((double)x): the double
  * result is within one double ulp of 2^x, so the final rounding is the correct one
  * unless 2^x lies within ~2^-52 (relative) of an fp32 rounding midpoint.  The tests
- * check, for every argument the softmax below can produce in [-128, 192), that this
- * agrees with a second route through long double (so the rounding is settled) and
- * with high-precision decimal arithmetic on samples.  The pages leave the exponential
+ * check, for every grid argument the softmax below can produce, that this agrees with
+ * a second route through long double (so the rounding is settled) and with
+ * high-precision decimal arithmetic on samples.  The pages leave the exponential
  * unspecified; the reading taken is the correctly rounded one. */
 float orc_exp2(float x) { return (float)exp2((double)x); }
+
+/* P' of a grid argument u: 2^(u - 80) rounded once to fp32 (u - 80 is exact in double;
+ * for u in [40, 160] it is also exact in fp32, so this is orc_exp2(u - 80) there). */
+float orc_p_of_u(float u) { return (float)exp2((double)u - 80.0); }
 
 /* INT8 code of one value: round half to even of fl32(x * r), clamped to [-127, 127]. */
 static int8_t i8_code(float x, float r) {
@@ -281,12 +285,13 @@ void orc_requant_v_cache(const int8_t* v_cache, const float* v_tok_scale, int H,
  *     scale * log2(e) (default fl32(fl32(1/sqrt(D)) * fl32(log2 e)));
  *     S_j = fl32(f32(acc_j) * c) is what the running max sees;
  *   - the exponent of each P is formed on a fixed grid:
- *         b  = fl32(200 - m_s)              (m_s = new max, or 0 if it is -inf)
+ *         b  = fl32(88 - m_s)               (m_s = new max, or 0 if it is -inf)
  *         u  = fl32(f32(acc_j) * c + b)     (one rounding: fused multiply-add)
- *         x  = fl32(u - 192)                (= S_j - m_s + 8, rounded to the grid of u)
- *         P' = 2^x  (correctly rounded fp32) = 256 * P
- *     so P' carries the exact 2^8 pre-scale that keeps FP8 P in the normal range, and
- *     x is a multiple of 2^-16 whenever |S_j - m_s| < 56;
+ *         P' = 2^(u - 80)  (correctly rounded fp32) = 256 * P
+ *     (u - 80 = S_j - m_s + 8, rounded to the grid of u) so P' carries the exact 2^8
+ *     pre-scale that keeps FP8 P in the normal range, and its exponent u - 80 is a
+ *     multiple of 2^-17 whenever S_j - m_s is in [-24, 40) (u in [64, 128)), which
+ *     holds for every P' with a nonzero e4m3 code;
  *   - alpha = 1 if the max did not change, else 2^(fl32(m - m_s)) (0 when m = -inf);
  *   - d' = fl32(alpha * d') + sum_j P'   (fp32; d is accumulated from P before the 8-bit
  *     conversion, as the page's order says; d' = 256 d);
@@ -351,15 +356,14 @@ void orc_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, const fl
       d = alpha * d;
       for (int c = 0; c < D; ++c) O[c] = alpha * O[c];
       /* P' and accumulate d (fp32 P, before the 8-bit conversion) */
-      float bconst = 200.0f - ms;
+      float bconst = 88.0f - ms;
       for (int jj = 0; jj < ORC_TILE; ++jj) {
         if (Sv[jj] == -INFINITY) { Pp[jj] = 0.0f; continue; }
         int j = j0 + jj;
         float sk = ks_per_token ? ks[j] : ks[j / ORC_TILE];
         float cc = (sq * sk) * lambda;
         float u = fmaf((float)acc[jj], cc, bconst);
-        float x = u - 192.0f;
-        Pp[jj] = orc_exp2(x);
+        Pp[jj] = orc_p_of_u(u);
       }
       for (int jj = 0; jj < ORC_TILE; ++jj) d = d + Pp[jj];
       /* convert P to 8 bit */
@@ -391,28 +395,24 @@ float orc_default_lambda(int D) {
   return inv * log2e;
 }
 
-/* Number of exp2 arguments x on the softmax grid in [lo_bits, hi_bits) of u (fp32 bit
- * patterns) for which (float)exp2((double)x) and (float)exp2l((long double)x) differ;
- * used by the tests to settle the rounding of orc_exp2 over the whole grid domain. */
+/* Number of grid arguments u in [lo_bits, hi_bits) (fp32 bit patterns) for which
+ * P' = 2^(u - 80) rounds differently through double and through long double; used by
+ * the tests to settle the rounding of orc_p_of_u over the whole grid domain. */
 long orc_exp2_check_grid(uint32_t lo_bits, uint32_t hi_bits) {
   long bad = 0;
   for (uint32_t ub = lo_bits; ub < hi_bits; ++ub) {
     float u = f_of_bits(ub);
-    float x = u - 192.0f;
-    float a = (float)exp2((double)x);
-    float b = (float)exp2l((long double)x);
+    float a = (float)exp2((double)u - 80.0);
+    float b = (float)exp2l((long double)u - 80.0L);
     if (bits_of_f(a) != bits_of_f(b)) bad++;
   }
   return bad;
 }
 
-/* E4M3 codes of 2^(u - 192) for all u with bit patterns in [lo_bits, hi_bits):
+/* E4M3 codes of P' = 2^(u - 80) for all u with bit patterns in [lo_bits, hi_bits):
  * the P8 code the softmax produces for every grid argument. */
 void orc_p8_codes_grid(uint32_t lo_bits, uint32_t hi_bits, uint8_t* codes) {
-  for (uint32_t ub = lo_bits; ub < hi_bits; ++ub) {
-    float x = f_of_bits(ub) - 192.0f;
-    codes[ub - lo_bits] = orc_e4m3_encode(orc_exp2(x));
-  }
+  for (uint32_t ub = lo_bits; ub < hi_bits; ++ub) codes[ub - lo_bits] = orc_e4m3_encode(orc_p_of_u(f_of_bits(ub)));
 }
 
 /* Array forms of the scalar codecs (for the tests). */

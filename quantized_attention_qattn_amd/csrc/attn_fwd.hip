@@ -58,16 +58,25 @@ constexpr int NBUF = 3;  // tile slots in LDS (loads run two slots ahead)
 [[maybe_unused]] constexpr int kVmcntZero = 0x0F70;
 constexpr int vmcnt_imm(int n) { return 0x0F70 | n; }
 [[maybe_unused]] constexpr int kLgkmcntZero = 0xC07F;
-// P' = 2^fl32(u - 192): the exponent argument on its fixed grid, evaluated with the
-// hardware exponential.  On this grid the e4m3 code of the result equals the code of
-// the correctly rounded power (checked over every fp32 u by qattn_p8_codes).
-__device__ __forceinline__ float p_from_u(float u) { return __builtin_amdgcn_exp2f(u - 192.0f); }
+// The softmax works with P'' = 2^u = 2^80 P', u = fl32(acc * c + fl32(88 - m)) being
+// the exponent argument on its fixed grid (2^-17 where P' can have a nonzero e4m3
+// code): one hardware exponential and no subtraction per key.  The 2^80 is exact and is
+// folded out by the FP8 conversion (its scale operand divides, exactly, for every
+// input) and once from d'' in the epilogue.  On this grid the e4m3 code of the result
+// equals the code of the correctly rounded power (checked over every fp32 u through
+// qattn_p8_codes).
+constexpr float kPScale = 0x1p80f;     // P'' / P'
+constexpr float kPScaleInv = 0x1p-80f;
+__device__ __forceinline__ float p_from_u(float u) { return __builtin_amdgcn_exp2f(u); }
+typedef short v2s_t __attribute__((ext_vector_type(2)));
 
-// Both halves of the word are written, so the first conversion may start from any
-// register (here a's bits) instead of a zeroed one.
+// e4m3 codes of P' = P'' / 2^80 for four values (bytes 0..3).  Both halves of the word
+// are written, so the first conversion may start from any register (here a's bits)
+// instead of a zeroed one.
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  v2s_t w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s_t, a), a, b, kPScale, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, kPScale, true);
+  return __builtin_bit_cast(int, w);
 }
 
 // Direct global -> LDS load of 16 bytes per lane: lane l of the wave writes LDS bytes
@@ -165,7 +174,8 @@ __device__ __forceinline__ float acc_f32(int biased) { return __builtin_bit_cast
 
 // Online-softmax update of one 64-key tile for this lane's query and its 32 keys
 // (key0 + i, i = 16 kb + j held in S_kb[j]).  Returns the 32 FP8 codes of P' = 256 P
-// packed as the B operand of the PV MFMA; updates m, the lane's share of d', and alpha.
+// packed as the B operand of the PV MFMA; updates m, the lane's share of d'' = 2^80 d',
+// and alpha.
 template <bool MASKED, bool PER_TOKEN>
 __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, const float* cp, float c_tile,
                                             int key0, int vis_last, float& m, float& dsum, float& alpha) {
@@ -206,10 +216,11 @@ __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, cons
   const float mnew = fmaxf(m, Mt);
   const float ms = mnew == -INFINITY ? 0.0f : mnew;
   alpha = mnew == m ? 1.0f : __builtin_amdgcn_exp2f(m - ms);
-  const float bconst = 200.0f - ms;
+  const float bconst = 88.0f - ms;  // u = S - m + 88: P' = 2^(u - 80) peaks at 2^8
   m = mnew;
   // four partial sums keep the additions off one dependent chain (the order of the
-  // additions into d' is not part of the contract; the result is an fp32 sum of P')
+  // additions into d' is not part of the contract; the result is an fp32 sum of P'',
+  // i.e. 2^80 times an fp32 sum of P')
   float ds[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   v8i pf;
 #pragma unroll
@@ -382,7 +393,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     if (PER_TOKEN) sC[t & 1][gtid >> 6][gtid & (BN - 1)] = (sq_mine * sKs[buf][gtid & (BN - 1)]) * a.lambda;
   };
   float m = -INFINITY;  // running max (log2 domain)
-  float dsum = 0.0f;    // this lane's share of d' (its 32 keys of every tile)
+  float dsum = 0.0f;    // this lane's share of d'' = 2^80 d' (its 32 keys of every tile)
   v16f O[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
@@ -530,7 +541,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   if (grp == 0) phase_barrier();
 
   // ---- epilogue: out = O * s_v / d' ----
-  const float dt = sum_with_partner(dsum);
+  const float dt = sum_with_partner(dsum) * kPScaleInv;  // d' = d'' / 2^80, exact
   if (qrow < a.Nq) {
     const int b = bh / a.H, h = bh - b * a.H;
     const int64_t off = b * a.out_sb + (int64_t)qrow * a.out_sn + h * a.out_sh;
@@ -562,7 +573,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
 __global__ void p8_codes_kernel(const float* u, uint8_t* codes, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    codes[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(p_from_u(u[i]), 0.0f, 0, false) & 0xff);
+    codes[i] = (uint8_t)(__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+                             v2s_t{0, 0}, p_from_u(u[i]), 0.0f, kPScale, false)) & 0xff);
 }
 
 template <int D>

@@ -129,13 +129,13 @@ def test_quant_v_every_bf16_value(qa):
 
 
 def test_p8_codes_whole_grid(qa):
-    """The fused kernel's P8 code of 2^(u - 192) equals the code of the correctly rounded
-    power (the oracle's) for EVERY fp32 u in [32, 200.5).  The kernel's argument is
-    u = fl32(acc * c + fl32(200 - m)) <= 200 + 2^-15, so this covers every argument with a
-    nonzero code (below u = 32, P' < 2^-160) and stays below e4m3's saturation point
-    (u > 200.86 gives P' > 464, where the hardware converter returns NaN)."""
-    lo = int(np.float32(32.0).view(np.uint32))
-    hi = int(np.float32(200.5).view(np.uint32))
+    """The fused kernel's P8 code of P' = 2^(u - 80) equals the code of the correctly
+    rounded power (the oracle's) for EVERY fp32 u in [16, 88.5).  The kernel's argument
+    is u = fl32(acc * c + fl32(88 - m)) <= 88 + 2^-16, so this covers every argument with
+    a nonzero code (below u = 16, P' < 2^-64) and stays below e4m3's saturation point
+    (u > 88.86 gives P' > 464, where the hardware converter returns NaN)."""
+    lo = int(np.float32(16.0).view(np.uint32))
+    hi = int(np.float32(88.5).view(np.uint32))
     say(f"p8 codes over {hi - lo} grid arguments")
     u = torch.arange(lo, hi, dtype=torch.int64, device="cuda").to(torch.int32).view(torch.float32)
     codes = torch.empty(hi - lo, dtype=torch.uint8, device="cuda")

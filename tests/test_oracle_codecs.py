@@ -104,9 +104,10 @@ def _exp2_cr_decimal(x: float) -> np.float32:
 
 def test_exp2_correctly_rounded_samples(orc):
     rng = np.random.default_rng(11)
-    # grid arguments x = fl32(u - 192) for random u in [64, 384), plus plain random x
-    u = rng.uniform(64.0, 200.0, 1500).astype(np.float32)  # x in [-128, 8]: P up to 256
-    x = np.concatenate([(u - np.float32(192.0)).astype(np.float32), rng.uniform(-30, 8, 500).astype(np.float32)])
+    # grid exponents x = u - 80 (exact in fp32) for random grid arguments u in [40, 88],
+    # plus plain random x
+    u = rng.uniform(40.0, 88.0, 1500).astype(np.float32)  # x in [-40, 8]: P up to 256
+    x = np.concatenate([(u - np.float32(80.0)).astype(np.float32), rng.uniform(-30, 8, 500).astype(np.float32)])
     got = orc.exp2(x)
     ref = np.array([_exp2_cr_decimal(v) for v in x], dtype=np.float32)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
@@ -114,27 +115,29 @@ def test_exp2_correctly_rounded_samples(orc):
 
 @pytest.mark.slow
 def test_exp2_grid_settled_by_long_double(orc):
-    """Over every softmax grid argument (all fp32 u in [64, 384)), the double route and
-    the long-double route round to the same fp32: the oracle's exp2 is correctly rounded
-    there (an ambiguous case would need 2^x within 2^-52 of an fp32 midpoint)."""
-    lo = int(np.float32(64.0).view(np.uint32))
-    hi = int(np.float32(384.0).view(np.uint32))
+    """Over every softmax grid argument (all fp32 u in [16, 96)), P' = 2^(u - 80) rounds
+    to the same fp32 through double and through long double: the oracle's P' is the
+    correctly rounded power there (an ambiguous case would need 2^(u - 80) within
+    2^-52 of an fp32 midpoint)."""
+    lo = int(np.float32(16.0).view(np.uint32))
+    hi = int(np.float32(96.0).view(np.uint32))
     assert orc.exp2_check_grid(lo, hi) == 0
 
 
 def test_p8_code_grid_properties(orc):
-    """P8 code of 2^(u - 192) is a monotone step function of u with the right anchors."""
-    lo = int(np.float32(64.0).view(np.uint32))
-    hi = int(np.float32(384.0).view(np.uint32))
+    """P8 code of 2^(u - 80) is a monotone step function of u with the right anchors."""
+    lo = int(np.float32(16.0).view(np.uint32))
+    hi = int(np.float32(96.0).view(np.uint32))
     codes = orc.p8_codes_grid(lo, hi)
     assert np.all(np.diff(codes.astype(np.int32)) >= 0)
     u = np.arange(lo, hi, dtype=np.uint32).view(np.float32)
     at = lambda val: codes[np.searchsorted(u, np.float32(val))]
-    assert at(200.0) == 0x78  # x = 8 -> 256
-    assert at(192.0) == 0x38  # x = 0 -> 1
-    assert at(192.0 - 9.0) == 0x01  # x = -9 -> 2^-9
-    assert at(192.0 - 11.0) == 0x00  # below half the smallest subnormal
-    assert codes.max() <= 0x7E  # the oracle saturates; the softmax never exceeds u = 200 + 2^-15
+    assert at(88.0) == 0x78  # x = 8 -> 256
+    assert at(80.0) == 0x38  # x = 0 -> 1
+    assert at(80.0 - 9.0) == 0x01  # x = -9 -> 2^-9
+    assert at(80.0 - 10.0) == 0x00  # 2^-10: half the smallest subnormal, ties to even (0)
+    assert at(80.0 - 11.0) == 0x00  # below half the smallest subnormal
+    assert codes.max() <= 0x7E  # the oracle saturates; the softmax never exceeds u = 88 + 2^-16
 
 
 def test_bf16_rounding(orc):
