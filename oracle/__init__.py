@@ -70,6 +70,11 @@ def lib():
             L.orc_requant_v_cache.restype = None
             L.orc_attn_rows.argtypes = [P, P, P, P, i32, P, i64, P, i32, i32, i32, f32, i32, i64, i32, i32, P]
             L.orc_attn_rows.restype = None
+            L.orc_attn_rows_part.argtypes = [P, P, P, P, i32, P, i64, i32, i32, i32, f32, i32, i64, i32, i32, i32,
+                                             i32, P, P, P]
+            L.orc_attn_rows_part.restype = None
+            L.orc_combine_rows.argtypes = [i32, P, P, P, P, i32, i32, P]
+            L.orc_combine_rows.restype = None
             L.orc_default_lambda.argtypes = [i32]
             L.orc_default_lambda.restype = f32
             L.orc_exp2_check_grid.argtypes = [_ct.c_uint32, _ct.c_uint32]
@@ -221,12 +226,26 @@ def _chunks(rows, chunk):
     return out
 
 
+def key_tiles(Nq: int, Nk: int, causal: bool, pos_off: int) -> int:
+    """Key tiles any query can see: ceil(min(Nk, Nq + pos_off) / 64) when causal."""
+    last = min(Nk, Nq + pos_off) if causal else Nk
+    return max(0, (last + TILE - 1) // TILE)
+
+
+def split_bounds(T: int, S: int):
+    """Split s of S covers key tiles [s*T//S, (s+1)*T//S) (see orc_combine_rows)."""
+    return [(s * T // S, (s + 1) * T // S) for s in range(S)]
+
+
 def attn(q8, q_scale, k8, k_scale, v8t, v_scale, Nq: int, Nk: int, lam: float, causal: bool = False,
-         pos_off: int | None = None, k_scale_per_token: bool = False, rows=None, workers: int | None = None):
+         pos_off: int | None = None, k_scale_per_token: bool = False, rows=None, workers: int | None = None,
+         kv_splits: int = 1):
     """Steps 3-5 on prequantized operands.
 
     q8 [B,H,Nq_pad,D]; q_scale [B,H,Nq_pad/64]; k8 [B,H,>=Nk,D]; k_scale [B,H,Nk_pad/64] or
     [B,H,Nk] (per token); v8t [B,H,D,ldv]; v_scale [B,H,D].
+    kv_splits > 1: the key tiles are cut into that many ranges, each run on its own, and
+    the partial results combined (orc_combine_rows).
     Returns fp32 out [B, len(rows), H, D] for the requested query rows (all rows if None).
     """
     B, H, _, D = q8.shape
@@ -253,12 +272,26 @@ def attn(q8, q_scale, k8, k_scale, v8t, v_scale, Nq: int, Nk: int, lam: float, c
             for (i0, i1) in _chunks(row_list, 16):
                 jobs.append((b, h, i0, i1))
 
+    bounds = split_bounds(key_tiles(Nq, Nk, causal, int(pos_off)), int(kv_splits)) if kv_splits > 1 else None
+
     def run(job):
         b, h, i0, i1 = job
         buf = np.empty((i1 - i0, D), dtype=np.float32)
-        L.orc_attn_rows(_ptr(q8[b, h]), _ptr(q_scale[b, h]), _ptr(k8[b, h]), _ptr(k_scale[b, h]),
-                        1 if k_scale_per_token else 0, _ptr(v8t[b, h]), ldv, _ptr(v_scale[b, h]), Nq, Nk, D,
-                        float(lam), 1 if causal else 0, int(pos_off), i0, i1, _ptr(buf))
+        if bounds is None:
+            L.orc_attn_rows(_ptr(q8[b, h]), _ptr(q_scale[b, h]), _ptr(k8[b, h]), _ptr(k_scale[b, h]),
+                            1 if k_scale_per_token else 0, _ptr(v8t[b, h]), ldv, _ptr(v_scale[b, h]), Nq, Nk, D,
+                            float(lam), 1 if causal else 0, int(pos_off), i0, i1, _ptr(buf))
+            return job, buf
+        S, n = len(bounds), i1 - i0
+        op = np.empty((S, n, D), dtype=np.float32)
+        mp = np.empty((S, n), dtype=np.float32)
+        dp = np.empty((S, n), dtype=np.float32)
+        for s, (t_lo, t_hi) in enumerate(bounds):
+            L.orc_attn_rows_part(_ptr(q8[b, h]), _ptr(q_scale[b, h]), _ptr(k8[b, h]), _ptr(k_scale[b, h]),
+                                 1 if k_scale_per_token else 0, _ptr(v8t[b, h]), ldv, Nq, Nk, D, float(lam),
+                                 1 if causal else 0, int(pos_off), i0, i1, t_lo, t_hi, _ptr(op[s]), _ptr(mp[s]),
+                                 _ptr(dp[s]))
+        L.orc_combine_rows(S, _ptr(op), _ptr(mp), _ptr(dp), _ptr(v_scale[b, h]), n, D, _ptr(buf))
         return job, buf
 
     with _cf.ThreadPoolExecutor(workers) as ex:
@@ -280,7 +313,8 @@ def fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, lam: float | None = None, c
 
 
 def fwd_i8kv(q: np.ndarray, k_cache: np.ndarray, k_tok_scale: np.ndarray, v_cache: np.ndarray,
-             v_tok_scale: np.ndarray, pos0: int, lam: float | None = None, rows=None, workers: int | None = None):
+             v_tok_scale: np.ndarray, pos0: int, lam: float | None = None, rows=None, workers: int | None = None,
+             kv_splits: int = 1):
     """Prefill over an int8 KV cache: q bf16 [Nq,H,D]; caches [H,Nk,D]; scales [H,Nk]."""
     Nq, H, D = q.shape
     Nk = k_cache.shape[1]
@@ -290,7 +324,7 @@ def fwd_i8kv(q: np.ndarray, k_cache: np.ndarray, k_tok_scale: np.ndarray, v_cach
     v8t, vs = requant_v_cache(v_cache, v_tok_scale)
     lam = default_lambda(D) if lam is None else lam
     out = attn(q8, qs, k_cache[None], k_tok_scale[None], v8t[None], vs[None], Nq, Nk, lam, causal=True,
-               pos_off=pos0, k_scale_per_token=True, rows=rows, workers=workers)
+               pos_off=pos0, k_scale_per_token=True, rows=rows, workers=workers, kv_splits=kv_splits)
     return out[0], dict(q8=q8[0], q_scale=qs[0], v8t=v8t, v_scale=vs, lam=lam)
 
 

@@ -301,6 +301,10 @@ void orc_requant_v_cache(const int8_t* v_cache, const float* v_tok_scale, int H,
  * fp32 sums of d' and O are formed here key by key in ascending order; their order is
  * not part of the contract (the GPU result is compared within a tolerance).
  *
+ * orc_attn_rows_part runs the tiles t_lo <= t < t_hi only and returns, per row, the
+ * unnormalized O (D values), the running max m (-inf if none of its keys is visible)
+ * and d'; orc_attn_rows runs all tiles and applies the epilogue.
+ *
  * Computes rows i0..i1-1 of one (b, h).
  *   q8:  int8 [Nq_pad, D] rows of this (b, h);  qs: fp32 [Nq_pad/64]
  *   k8:  int8 rows of this (b, h), row stride D (at least Nk rows);
@@ -309,12 +313,14 @@ void orc_requant_v_cache(const int8_t* v_cache, const float* v_tok_scale, int H,
  *   causal: key j visible iff j <= i + pos_off (pos_off = Nk - Nq for bottom-right
  *           alignment, = pos0 for a prefill chunk starting at position pos0)
  *   out: fp32 [i1 - i0][D]. */
-void orc_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks, int ks_per_token,
-                   const uint8_t* v8t, int64_t ldv, const float* vs, int Nq, int Nk, int D, float lambda,
-                   int causal, int64_t pos_off, int i0, int i1, float* out) {
+void orc_attn_rows_part(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks, int ks_per_token,
+                        const uint8_t* v8t, int64_t ldv, int Nq, int Nk, int D, float lambda, int causal,
+                        int64_t pos_off, int i0, int i1, int t_lo, int t_hi, float* o_out, float* m_out,
+                        float* d_out) {
   (void)Nq;
   e4m3_init();
   int ntile = (Nk + ORC_TILE - 1) / ORC_TILE;
+  if (t_hi > ntile) t_hi = ntile;
   float* O = (float*)malloc(sizeof(float) * D);
   float* Pp = (float*)malloc(sizeof(float) * ORC_TILE);
   float* Sv = (float*)malloc(sizeof(float) * ORC_TILE);
@@ -329,7 +335,7 @@ void orc_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, const fl
     float sq = qs[i / ORC_TILE];
     float m = -INFINITY, d = 0.0f;
     for (int c = 0; c < D; ++c) O[c] = 0.0f;
-    for (int t = 0; t < ntile; ++t) {
+    for (int t = t_lo; t < t_hi; ++t) {
       int j0 = t * ORC_TILE;
       /* skip tiles with no visible key for this row (a no-op for m, d and O) */
       int64_t last_vis = causal ? (int64_t)i + pos_off : (int64_t)Nk - 1;
@@ -382,10 +388,61 @@ void orc_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, const fl
       }
       m = mnew;
     }
-    float* o = out + (int64_t)(i - i0) * D;
-    for (int c = 0; c < D; ++c) o[c] = (d == 0.0f) ? 0.0f : (O[c] * vs[c]) / d;
+    float* o = o_out + (int64_t)(i - i0) * D;
+    for (int c = 0; c < D; ++c) o[c] = O[c];
+    m_out[i - i0] = m;
+    d_out[i - i0] = d;
   }
   free(O); free(Pp); free(Sv); free(acc); free(P8); free(vdec);
+}
+
+/* All tiles, then the epilogue out_c = fl32(fl32(O_c * s_v[c]) / d'), 0 if d' = 0. */
+void orc_attn_rows(const int8_t* q8, const float* qs, const int8_t* k8, const float* ks, int ks_per_token,
+                   const uint8_t* v8t, int64_t ldv, const float* vs, int Nq, int Nk, int D, float lambda,
+                   int causal, int64_t pos_off, int i0, int i1, float* out) {
+  int n = i1 - i0;
+  float* O = (float*)malloc(sizeof(float) * (size_t)n * D);
+  float* mv = (float*)malloc(sizeof(float) * (size_t)n);
+  float* dv = (float*)malloc(sizeof(float) * (size_t)n);
+  orc_attn_rows_part(q8, qs, k8, ks, ks_per_token, v8t, ldv, Nq, Nk, D, lambda, causal, pos_off, i0, i1, 0,
+                     (Nk + ORC_TILE - 1) / ORC_TILE, O, mv, dv);
+  for (int r = 0; r < n; ++r)
+    for (int c = 0; c < D; ++c)
+      out[(int64_t)r * D + c] = (dv[r] == 0.0f) ? 0.0f : (O[(int64_t)r * D + c] * vs[c]) / dv[r];
+  free(O); free(mv); free(dv);
+}
+
+/* Split-KV combine (the reading taken for splitting the key range of few-query prefill;
+ * the pages' kernels run one pass): the key tiles [0, T) are cut into S contiguous
+ * ranges [s T / S, (s + 1) T / S); each range runs the loop above from m = -inf,
+ * d' = 0, O = 0 and leaves (O_s, m_s, d'_s).  Per row, in split order s = 0 .. S-1:
+ *     M = max_s m_s                          (all -inf: the row outputs zeros)
+ *     w_s = 2^(fl32(m_s - M)) correctly rounded (0 when m_s = -inf)
+ *     d' = sum_s fl32(w_s * d'_s),  O_c = sum_s fl32(w_s * O_s,c)   (fp32, in order)
+ *     out_c = fl32(fl32(O_c * s_v[c]) / d'), 0 if d' = 0.
+ * o_part [S][n][D], m_part and d_part [S][n]; out [n][D]. */
+void orc_combine_rows(int S, const float* o_part, const float* m_part, const float* d_part, const float* vs, int n,
+                      int D, float* out) {
+  for (int r = 0; r < n; ++r) {
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s)
+      if (m_part[(int64_t)s * n + r] > M) M = m_part[(int64_t)s * n + r];
+    float* o = out + (int64_t)r * D;
+    if (M == -INFINITY) {
+      for (int c = 0; c < D; ++c) o[c] = 0.0f;
+      continue;
+    }
+    float d = 0.0f;
+    for (int c = 0; c < D; ++c) o[c] = 0.0f;
+    for (int s = 0; s < S; ++s) {
+      float ms = m_part[(int64_t)s * n + r];
+      float w = (ms == -INFINITY) ? 0.0f : orc_exp2(ms - M);
+      d = d + w * d_part[(int64_t)s * n + r];
+      const float* os = o_part + ((int64_t)s * n + r) * D;
+      for (int c = 0; c < D; ++c) o[c] = o[c] + w * os[c];
+    }
+    for (int c = 0; c < D; ++c) o[c] = (d == 0.0f) ? 0.0f : (o[c] * vs[c]) / d;
+  }
 }
 
 /* Default lambda for head dim D: fl32(fl32(1/sqrt(D)) * fl32(log2 e)). */
