@@ -172,7 +172,9 @@ def main():
         dq = dev_bf16(q)
         dkc, dkts = torch.from_numpy(kc).to(dev), torch.from_numpy(kts).to(dev)
         dvc, dvts = torch.from_numpy(vc).to(dev), torch.from_numpy(vts).to(dev)
-        ws = torch.empty(qa.qattn_fwd_i8kv_workspace_bytes(w.H, w.Nq, w.Nk, w.D), dtype=torch.uint8, device=dev)
+        kv_splits = qa.qattn_fwd_i8kv_kv_splits(w.H, w.Nq, w.Nk, w.pos0)  # the library's rule
+        ws = torch.empty(qa.qattn_fwd_i8kv_workspace_bytes(w.H, w.Nq, w.Nk, w.D, kv_splits), dtype=torch.uint8,
+                         device=dev)
         out = torch.empty((w.Nq, w.H, w.D), dtype=torch.bfloat16, device=dev)
         ev_pairs = []
 
@@ -219,6 +221,7 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 inputs; see workloads.py)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.Nq, "N_k": w.Nk, "D": w.D,
                    "causal": w.causal, "pos0": w.pos0 if w.kind == "i8kv" else None,
+                   "kv_splits": kv_splits if w.kind == "i8kv" else 1,
                    "step": "quant_qk + quant_v + fwd" if w.kind == "dense" else "fwd_i8kv (incl. q quant, V requant)",
                    "input_sha256": in_sha},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel" if w.kind == "dense" else "fwd_i8kv call",

@@ -97,17 +97,32 @@ int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const fl
  *      receives the per-channel e4m3 requantization of V (fl32(code * scale) quantized
  *      as in step 2 over all Nk tokens) and the INT8 blocks of q (as in step 1, no
  *      smoothing).
+ *   kv_splits: split-KV for few queries over a long context.  The key tiles
+ *      [0, T), T = ceil(min(Nk, pos0 + Nq) / 64), are cut into kv_splits contiguous ranges
+ *      [s T / S, (s + 1) T / S); each range runs the loop above on its own (from
+ *      m = -inf, d' = 0, O = 0) and a second kernel combines the ranges of every row in
+ *      range order: M = max m_s, w_s = 2^(m_s - M), out = (sum w_s O_s) * s_v /
+ *      (sum w_s d'_s).  1 = one pass; 0 = the count qattn_fwd_i8kv_kv_splits returns;
+ *      at most 64.
  *   out: [Nq, H, D] view with strides out_str = {sn, sh}.
  * K codes are used as stored, with c_j = fl32(fl32(s_q * s_k[j]) * scale_log2). */
 int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache, const float* k_tok_scale,
                    const int8_t* v_cache, const float* v_tok_scale, int H, int Nq, int Nk, int D, int pos0,
-                   float scale_log2, void* workspace, size_t workspace_bytes, void* out, const int64_t out_str[2],
-                   int out_dtype, void* stream);
+                   float scale_log2, int kv_splits, void* workspace, size_t workspace_bytes, void* out,
+                   const int64_t out_str[2], int out_dtype, void* stream);
 
-/* Workspace size for qattn_fwd_i8kv: H*D*Nk_pad (e4m3 V) + H*D*4 (V scales) +
- * H*Nq_pad*D (q codes) + H*Nq_pad/64*4 (q scales), each section rounded up to 256 bytes.
- * Returns 0 for invalid sizes. */
-size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D);
+/* Workspace size for qattn_fwd_i8kv with kv_splits key ranges (1 .. 64; resolve 0 with
+ * qattn_fwd_i8kv_kv_splits first): H*D*Nk_pad (e4m3 V) + H*D*4 (V scales) + H*Nq_pad*D
+ * (q codes) + H*Nq_pad/64*4 (q scales), and for kv_splits > 1 the partial results
+ * kv_splits*H*Nq_pad*D*4 (O) + kv_splits*H*Nq_pad*8 (m, d'), each section rounded up to
+ * 256 bytes.  Returns 0 for invalid sizes. */
+size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D, int kv_splits);
+
+/* The key-range count qattn_fwd_i8kv uses for kv_splits = 0 (host only, no GPU call):
+ * ceil(512 / (H * ceil(Nq / 256))) -- about two workgroups per CU -- capped so that every
+ * range holds at least 16 key tiles and at 64, at least 1.  Returns 0 for invalid sizes
+ * (0 <= pos0, pos0 + Nq <= Nk). */
+int qattn_fwd_i8kv_kv_splits(int H, int Nq, int Nk, int pos0);
 
 /* Self-test hook: codes[i] = E4M3(2^(u[i] - 80)) computed by the fused kernel's own
  * device functions (the FP8 P code the softmax produces for the grid argument u: the

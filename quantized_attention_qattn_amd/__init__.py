@@ -4,7 +4,7 @@ The functions below carry the C-ABI's names and only marshal arguments: torch te
 device pointers, element strides and the current HIP stream go to ``libqattn.so``;
 every step of the computation runs in the library's HIP kernels.  torch provides the
 device memory and the stream, nothing else.  Importing this package fails loudly when
-the library has not been built (``python -m quantized_attention_qattn_amd._build``);
+the library has not been built (``python quantized_attention_qattn_amd/_build.py``);
 there is no fallback.
 
 Layouts (N_pad = ceil(N / 64) * 64):
@@ -29,7 +29,7 @@ QATTN_OUT_BF16, QATTN_OUT_F32 = 0, 1
 BLOCK = 64
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_attention_qattn_amd._build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python quantized_attention_qattn_amd/_build.py`")
 
 _lib = _ct.CDLL(LIB_PATH)
 _P, _I, _I64, _F, _SZ = _ct.c_void_p, _ct.c_int, _ct.c_int64, _ct.c_float, _ct.c_size_t
@@ -41,10 +41,12 @@ _lib.qattn_quant_v.argtypes = [_P, _I64x3, _I, _I, _I, _I, _P, _P, _P]
 _lib.qattn_quant_v.restype = _I
 _lib.qattn_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I64x3, _I, _P]
 _lib.qattn_fwd.restype = _I
-_lib.qattn_fwd_i8kv.argtypes = [_P, _I64x2, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _SZ, _P, _I64x2, _I, _P]
+_lib.qattn_fwd_i8kv.argtypes = [_P, _I64x2, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P, _I64x2, _I, _P]
 _lib.qattn_fwd_i8kv.restype = _I
-_lib.qattn_fwd_i8kv_workspace_bytes.argtypes = [_I, _I, _I, _I]
+_lib.qattn_fwd_i8kv_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.qattn_fwd_i8kv_workspace_bytes.restype = _SZ
+_lib.qattn_fwd_i8kv_kv_splits.argtypes = [_I, _I, _I, _I]
+_lib.qattn_fwd_i8kv_kv_splits.restype = _I
 _lib.qattn_p8_codes.argtypes = [_P, _P, _I64, _P]
 _lib.qattn_p8_codes.restype = _I
 _lib.qattn_status_string.argtypes = [_I]
@@ -142,12 +144,16 @@ def qattn_fwd(q8, q_scale, k8, k_scale, v8t, v_scale, Nq: int, Nk: int, out, sca
                           _stream(stream)), "qattn_fwd")
 
 
-def qattn_fwd_i8kv_workspace_bytes(H: int, Nq: int, Nk: int, D: int) -> int:
-    return int(_lib.qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D))
+def qattn_fwd_i8kv_workspace_bytes(H: int, Nq: int, Nk: int, D: int, kv_splits: int) -> int:
+    return int(_lib.qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, kv_splits))
+
+
+def qattn_fwd_i8kv_kv_splits(H: int, Nq: int, Nk: int, pos0: int) -> int:
+    return int(_lib.qattn_fwd_i8kv_kv_splits(H, Nq, Nk, pos0))
 
 
 def qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, workspace, out,
-                   scale_log2: float = 0.0, stream=None) -> None:
+                   scale_log2: float = 0.0, stream=None, kv_splits: int = 0) -> None:
     _need(q, torch.bfloat16, "q")
     Nq, H, D = q.shape
     Nk = k_cache.shape[1]
@@ -161,7 +167,8 @@ def qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, wor
         raise ValueError(f"out: expected a CUDA [Nq, H, D] = {(Nq, H, D)} view with unit channel stride")
     od = QATTN_OUT_BF16 if out.dtype == torch.bfloat16 else QATTN_OUT_F32 if out.dtype == torch.float32 else -1
     _check(_lib.qattn_fwd_i8kv(_ptr(q), _I64x2(*q.stride()[:2]), _ptr(k_cache), _ptr(k_tok_scale), _ptr(v_cache),
-                               _ptr(v_tok_scale), H, Nq, Nk, D, int(pos0), float(scale_log2), _ptr(workspace),
+                               _ptr(v_tok_scale), H, Nq, Nk, D, int(pos0), float(scale_log2), int(kv_splits),
+                               _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _ptr(out), _I64x2(*out.stride()[:2]), od,
                                _stream(stream)), "qattn_fwd_i8kv")
 
@@ -218,11 +225,14 @@ def attention(q, k, v, causal: bool = False, scale_log2: float = 0.0, out_dtype=
 
 
 def attention_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, scale_log2: float = 0.0,
-                   out_dtype=torch.bfloat16, stream=None):
+                   out_dtype=torch.bfloat16, stream=None, kv_splits: int = 0):
+    """kv_splits = 0: the library's rule (qattn_fwd_i8kv_kv_splits)."""
     Nq, H, D = q.shape
-    ws = torch.empty(qattn_fwd_i8kv_workspace_bytes(H, Nq, k_cache.shape[1], D), dtype=torch.uint8, device=q.device)
+    Nk = k_cache.shape[1]
+    S = kv_splits if kv_splits > 0 else qattn_fwd_i8kv_kv_splits(H, Nq, Nk, pos0)
+    ws = torch.empty(qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, S), dtype=torch.uint8, device=q.device)
     out = torch.empty((Nq, H, D), dtype=out_dtype, device=q.device)
-    qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0, ws, out, scale_log2, stream)
+    qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0, ws, out, scale_log2, stream, kv_splits=S)
     return out, ws
 
 

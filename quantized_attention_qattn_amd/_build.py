@@ -1,5 +1,8 @@
 """Build libqattn.so in-tree with hipcc for gfx950.
 
+Run as a file (``python quantized_attention_qattn_amd/_build.py``) or load it by path:
+importing it through the package would first load the library being rebuilt.
+
 Every HIP source is compiled with ``-ffp-contract=off`` (the numeric contract spells out
 each fused multiply-add) and with packed fp32 instructions disabled.
 """

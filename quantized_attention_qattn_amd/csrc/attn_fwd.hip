@@ -52,7 +52,7 @@ namespace detail {
 constexpr int BM = 256;  // query rows per workgroup
 [[maybe_unused]] constexpr int BN = 64;   // keys per tile (the numeric contract's tile)
 constexpr int NT = 512;  // threads per workgroup (8 waves)
-constexpr int NBUF = 3;  // tile slots in LDS (loads run two slots ahead)
+[[maybe_unused]] constexpr int NBUF = 3;  // tile slots in LDS (loads run two slots ahead)
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
 // vmcnt_hi[15:14]): vmcnt(n < 16) with the others at their maxima, and lgkmcnt(0).
 [[maybe_unused]] constexpr int kVmcntZero = 0x0F70;
@@ -66,7 +66,7 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | n; }
 // equals the code of the correctly rounded power (checked over every fp32 u through
 // qattn_p8_codes).
 constexpr float kPScale = 0x1p80f;     // P'' / P'
-constexpr float kPScaleInv = 0x1p-80f;
+[[maybe_unused]] constexpr float kPScaleInv = 0x1p-80f;
 __device__ __forceinline__ float p_from_u(float u) { return __builtin_amdgcn_exp2f(u); }
 typedef short v2s_t __attribute__((ext_vector_type(2)));
 
@@ -280,9 +280,13 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int nqb = (a.Nq + BM - 1) / BM;
   // wave-uniform by construction; readfirstlane lets the compiler keep it in SGPRs
+  // work = ((bh * kv_splits + split) * nqb + qblk): workgroups that stream the same key
+  // range of one (b, h) are neighbours, so an XCD's L2 serves all their query blocks
   const int work = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
-  const int bh = __builtin_amdgcn_readfirstlane(work / nqb);
-  const int qblk = work - bh * nqb;
+  const int rest = __builtin_amdgcn_readfirstlane(work / nqb);
+  const int qblk = work - rest * nqb;
+  const int bh = __builtin_amdgcn_readfirstlane(rest / a.kv_splits);
+  const int split = rest - bh * a.kv_splits;
   const int q0 = qblk * BM;
   const int qw = q0 + 32 * wave;  // first row of this wave
   const int qrow = qw + l32;      // this lane's query row
@@ -307,6 +311,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     sq_mine = a.q_scale[bh * a.qs_bh + q0 / kBlk + (gtid >> 6)];
 
   // tiles streamed by the workgroup, and tiles holding a key visible to this wave
+  // (absolute tile indices), then restricted to this workgroup's key range: the loop
+  // below runs tiles t0 + i, i = 0 .. ntiles - 1
   int ntiles = (a.Nk + BN - 1) / BN;
   int wtiles = wave_live ? ntiles : 0;
   if (CAUSAL) {
@@ -317,7 +323,10 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     if (wlast > a.Nk - 1) wlast = a.Nk - 1;
     wtiles = (!wave_live || wlast < 0) ? 0 : (int)(wlast / BN) + 1;
   }
-  wtiles = __builtin_amdgcn_readfirstlane(wtiles);
+  const int t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * a.tiles_total / a.kv_splits));
+  const int t_end = (int)((int64_t)(split + 1) * a.tiles_total / a.kv_splits);
+  ntiles = __builtin_amdgcn_readfirstlane(max(0, min(ntiles, t_end) - t0));
+  wtiles = __builtin_amdgcn_readfirstlane(max(0, min(wtiles, t_end) - t0));
 
   // ---- staging: global -> LDS directly (buffer loads with the LDS destination) ----
   // Each group-0 wave fills PT 1 KiB segments of the K tile and of the V^T code tile;
@@ -348,13 +357,13 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   // LDS byte addresses of the buffers, formed once (wave-uniform)
   const uint32_t ldsK0 = lds_addr(&sK[0][0]), ldsV0 = lds_addr(&sV[0][0]), ldsKs0 = lds_addr(&sKs[0][0]);
   auto stage = [&](int t, int buf) {
-    if (PER_TOKEN && t < ntiles) dma_4B(srs, ldsKs0 + buf * (4 * BN), 4 * lane, 4 * t * BN);
+    if (PER_TOKEN && t < ntiles) dma_4B(srs, ldsKs0 + buf * (4 * BN), 4 * lane, 4 * (t0 + t) * BN);
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       // wave-uniform; readfirstlane tells the compiler so (the asm needs an SGPR)
       const uint32_t seg = __builtin_amdgcn_readfirstlane(1024u * ((wave & 3) * PT + i));
-      if (t < ntiles) dma_16B(krs, ldsK0 + buf * (BN * D) + seg, koff[i], t * BN * D);
-      if (t > 0) dma_16B(vrs, ldsV0 + buf * (D * BN) + seg, voff[i], (t - 1) * BN);
+      if (t < ntiles) dma_16B(krs, ldsK0 + buf * (BN * D) + seg, koff[i], (t0 + t) * BN * D);
+      if (t > 0) dma_16B(vrs, ldsV0 + buf * (D * BN) + seg, voff[i], (t0 + t - 1) * BN);
     }
   };
   // wait until at most the loads of slot t are in flight (t > ntiles: none)
@@ -424,7 +433,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   const __attribute__((address_space(4))) float* ks_const =
       (const __attribute__((address_space(4))) float*)uniform_ptr(a.k_scale + bh * a.ks_bh);
   const int nkb = (a.Nk + BN - 1) / BN;  // K scale blocks
-  float ks_next = (!PER_TOKEN && ntiles > 0) ? ks_const[0] : 0.0f;
+  float ks_next = (!PER_TOKEN && ntiles > 0) ? ks_const[t0] : 0.0f;
   if (grp == 1) phase_barrier();
   int buf = 0;  // buffer of slot i
   for (int i = 0; i <= ntiles; ++i) {
@@ -503,11 +512,12 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     // next one: uniform addresses read through the constant address space, i.e. scalar
     // loads, issued a phase ahead so that their latency is never waited for
     const float ks_cur = ks_next;
-    if (!PER_TOKEN && i + 1 < nkb) ks_next = ks_const[i + 1];
+    if (!PER_TOKEN && t0 + i + 1 < nkb) ks_next = ks_const[t0 + i + 1];
     if (i < wtiles) {
-      const int key0 = i * BN + 32 * hh;
+      const int ti = t0 + i;  // absolute tile
+      const int key0 = ti * BN + 32 * hh;
       const bool masked =
-          (i * BN + BN > a.Nk) || (CAUSAL && (int64_t)i * BN + BN - 1 > (int64_t)qw + a.pos_off);
+          (ti * BN + BN > a.Nk) || (CAUSAL && (int64_t)ti * BN + BN - 1 > (int64_t)qw + a.pos_off);
       const float c_tile = PER_TOKEN ? 0.0f : (sq_w * ks_cur) * a.lambda;
       const float* cp = &sC[i & 1][wave >> 1][32 * hh];
       float alpha;
@@ -542,7 +552,20 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
 
   // ---- epilogue: out = O * s_v / d' ----
   const float dt = sum_with_partner(dsum) * kPScaleInv;  // d' = d'' / 2^80, exact
-  if (qrow < a.Nq) {
+  if (a.kv_splits > 1) {  // partial result of this key range, combined by attn_combine_kernel
+    if (qrow < a.Nq) {
+      const int64_t prow = ((int64_t)split * (a.B * a.H) + bh) * a.nq_pad + qrow;
+      float* po = a.part_o + prow * D;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c0 = 32 * s + 8 * g + 4 * hh;
+          *(float4*)(po + c0) = make_float4(O[s][4 * g], O[s][4 * g + 1], O[s][4 * g + 2], O[s][4 * g + 3]);
+        }
+      if (hh == 0) *(float2*)(a.part_md + 2 * prow) = make_float2(m, dt);
+    }
+  } else if (qrow < a.Nq) {
     const int b = bh / a.H, h = bh - b * a.H;
     const int64_t off = b * a.out_sb + (int64_t)qrow * a.out_sn + h * a.out_sh;
     const float* vs = a.v_scale + (int64_t)bh * D;
@@ -577,9 +600,54 @@ __global__ void p8_codes_kernel(const float* u, uint8_t* codes, int64_t n) {
                              v2s_t{0, 0}, p_from_u(u[i]), 0.0f, kPScale, false)) & 0xff);
 }
 
+// Split-KV combine: one thread per (b, h, query row, 4 channels).  Per row, in split
+// order: M = max m_s; w_s = 2^(m_s - M) (0 for a range with no visible key); d' =
+// sum w_s d'_s and O_c = sum w_s O_s,c in fp32; out_c = (O_c * s_v[c]) / d' (0 if d' = 0).
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(FwdArgs a) {
+  constexpr int G = D / 4;  // channel groups per row
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t rows = (int64_t)a.B * a.H * a.Nq;
+  if (t >= rows * G) return;
+  const int g = (int)(t % G);
+  const int64_t r = t / G;  // (bh, row)
+  const int bh = (int)(r / a.Nq), row = (int)(r - (int64_t)bh * a.Nq);
+  const int S = a.kv_splits;
+  const int64_t BH = (int64_t)a.B * a.H;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_md[2 * ((s * BH + bh) * a.nq_pad + row)]);
+  float d = 0.0f, o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const int64_t prow = (s * BH + bh) * a.nq_pad + row;
+      const float2 md = *(const float2*)(a.part_md + 2 * prow);
+      const float w = md.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(md.x - M);
+      d = d + w * md.y;
+      const float4 po = *(const float4*)(a.part_o + prow * D + 4 * g);
+      o0 = o0 + w * po.x;
+      o1 = o1 + w * po.y;
+      o2 = o2 + w * po.z;
+      o3 = o3 + w * po.w;
+    }
+  }
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int c0 = 4 * g;
+  const float* vs = a.v_scale + (int64_t)bh * D;
+  const float o[4] = {d == 0.0f ? 0.0f : (o0 * vs[c0]) / d, d == 0.0f ? 0.0f : (o1 * vs[c0 + 1]) / d,
+                      d == 0.0f ? 0.0f : (o2 * vs[c0 + 2]) / d, d == 0.0f ? 0.0f : (o3 * vs[c0 + 3]) / d};
+  const int64_t off = b * a.out_sb + (int64_t)row * a.out_sn + h * a.out_sh + c0;
+  if (a.out_bf16) {
+    const uint32_t w0 = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+    const uint32_t w1 = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+    *(uint2*)((uint16_t*)a.out + off) = make_uint2(w0, w1);
+  } else {
+    *(float4*)((float*)a.out + off) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
-  const int grid = a.B * a.H * ((a.Nq + BM - 1) / BM);
+  const int grid = a.B * a.H * ((a.Nq + BM - 1) / BM) * a.kv_splits;
   if (a.per_token) {
     if (a.causal)
       attn_fwd_kernel<D, true, true><<<grid, NT, 0, st>>>(a);
@@ -590,6 +658,12 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
       attn_fwd_kernel<D, false, true><<<grid, NT, 0, st>>>(a);
     else
       attn_fwd_kernel<D, false, false><<<grid, NT, 0, st>>>(a);
+  }
+  if (a.kv_splits > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t threads = (int64_t)a.B * a.H * a.Nq * (D / 4);
+    attn_combine_kernel<D><<<(int)((threads + 255) / 256), 256, 0, st>>>(a);
   }
   return hipGetLastError();
 }

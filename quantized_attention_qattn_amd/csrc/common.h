@@ -86,8 +86,15 @@ struct FwdArgs {
   float lambda;
   int64_t pos_off;  // causal: key j visible to query i iff j <= i + pos_off
   int causal, per_token, out_bf16;
+  // Split-KV: the key tiles [0, tiles_total) are cut into kv_splits contiguous ranges
+  // [s T / S, (s + 1) T / S); with kv_splits > 1 each (b, h, query block, range) writes
+  // its unnormalized O and (m, d') to part_o / part_md and the combine kernel forms the
+  // output.  kv_splits = 1: one pass over all tiles, output written directly.
+  int kv_splits, tiles_total;
+  float* part_o;   // [kv_splits][B*H][nq_pad][D]
+  float* part_md;  // [kv_splits][B*H][nq_pad][2]: m (log2 domain, -inf if none), d'
 };
-hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st);
+hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st);  // both kernels when split
 hipError_t launch_p8_codes(const float* u, uint8_t* codes, int64_t n, hipStream_t st);
 
 }  // namespace qattn

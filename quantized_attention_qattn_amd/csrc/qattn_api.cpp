@@ -1,6 +1,8 @@
 // C-ABI entry points of libqattn: argument validation (before any HIP call) and launch
 // sequencing on the caller's stream.  No allocation, no synchronization.
 #include <math.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -13,6 +15,11 @@ namespace {
 
 constexpr int64_t kMaxN = (int64_t)1 << 28;  // keeps every row index and grid size in range
 constexpr int kMaxGridYZ = 65535;
+// Split-KV rule for the prefill entry point: enough key ranges for about two waves of
+// workgroups over the 256 CUs, each range at least kSplitMinTiles key tiles long.
+constexpr int64_t kSplitTargetWorkgroups = 512;
+constexpr int64_t kSplitMinTiles = 16;
+constexpr int kMaxKvSplits = 64;
 
 inline int64_t npad64(int64_t n) { return (n + kBlk - 1) / kBlk * kBlk; }
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -141,21 +148,43 @@ int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const fl
   a.causal = causal ? 1 : 0;
   a.per_token = 0;
   a.out_bf16 = out_dtype == QATTN_OUT_BF16;
+  a.kv_splits = 1;
+  a.tiles_total = (int)(nkp / kBlk);
   return status_of(launch_attn_fwd(a, D, (hipStream_t)stream));
 }
 
-size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D) {
+// Key tiles a causal prefill reads: every query sees keys 0 .. pos0 + i.
+static int64_t i8kv_key_tiles(int Nq, int Nk, int pos0) {
+  const int64_t last = std::min<int64_t>(Nk, (int64_t)pos0 + Nq);
+  return (last + kBlk - 1) / kBlk;
+}
+
+int qattn_fwd_i8kv_kv_splits(int H, int Nq, int Nk, int pos0) {
+  if (H <= 0 || Nq <= 0 || Nk <= 0 || pos0 < 0 || (int64_t)pos0 + Nq > Nk) return 0;
+  const int64_t wgs = (int64_t)H * ((Nq + 255) / 256);  // workgroups of one pass
+  const int64_t T = i8kv_key_tiles(Nq, Nk, pos0);
+  int64_t S = (kSplitTargetWorkgroups + wgs - 1) / wgs;
+  S = std::min<int64_t>(S, T / kSplitMinTiles);
+  S = std::min<int64_t>(S, kMaxKvSplits);
+  return (int)std::max<int64_t>(S, 1);
+}
+
+size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D, int kv_splits) {
   if (H <= 0 || Nq <= 0 || Nk <= 0 || H > kMaxGridYZ || Nq > kMaxN || Nk > kMaxN) return 0;
   if (D != 64 && D != 128) return 0;
+  if (kv_splits < 1 || kv_splits > kMaxKvSplits) return 0;
   const size_t nkp = (size_t)npad64(Nk), nqp = (size_t)npad64(Nq);
-  return round256((size_t)H * D * nkp) + round256((size_t)H * D * 4) + round256((size_t)H * nqp * D) +
-         round256((size_t)H * (nqp / kBlk) * 4);
+  size_t bytes = round256((size_t)H * D * nkp) + round256((size_t)H * D * 4) + round256((size_t)H * nqp * D) +
+                 round256((size_t)H * (nqp / kBlk) * 4);
+  if (kv_splits > 1)
+    bytes += round256((size_t)kv_splits * H * nqp * D * 4) + round256((size_t)kv_splits * H * nqp * 2 * 4);
+  return bytes;
 }
 
 int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache, const float* k_tok_scale,
                    const int8_t* v_cache, const float* v_tok_scale, int H, int Nq, int Nk, int D, int pos0,
-                   float scale_log2, void* workspace, size_t workspace_bytes, void* out, const int64_t out_str[2],
-                   int out_dtype, void* stream) {
+                   float scale_log2, int kv_splits, void* workspace, size_t workspace_bytes, void* out,
+                   const int64_t out_str[2], int out_dtype, void* stream) {
   if (!k_cache || !k_tok_scale || !v_cache || !v_tok_scale || !workspace) return QATTN_EINVAL;
   if (!bf16_view_ok(q, q_str, 2)) return QATTN_EINVAL;
   if (!sizes_ok(1, H, Nq) || !sizes_ok(1, H, Nk)) return QATTN_EINVAL;
@@ -166,7 +195,12 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
   if (!aligned(workspace, 256)) return QATTN_EINVAL;
   if (!out_ok(out, out_str, 2, out_dtype)) return QATTN_EINVAL;
   if (isnan(scale_log2) || isinf(scale_log2)) return QATTN_EINVAL;
-  if (workspace_bytes < qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D)) return QATTN_EWORKSPACE;
+  if (kv_splits == 0) kv_splits = qattn_fwd_i8kv_kv_splits(H, Nq, Nk, pos0);
+  if (kv_splits < 1 || kv_splits > kMaxKvSplits) return QATTN_EINVAL;
+  if ((int64_t)H * ((Nq + 255) / 256) * kv_splits > INT32_MAX) return QATTN_EINVAL;
+  const size_t need = qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, kv_splits);
+  if (need == 0) return QATTN_EINVAL;
+  if (workspace_bytes < need) return QATTN_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int64_t nkp = npad64(Nk), nqp = npad64(Nq);
   uint8_t* ws = (uint8_t*)workspace;
@@ -177,6 +211,14 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
   int8_t* q8 = (int8_t*)ws;
   ws += round256((size_t)H * nqp * D);
   float* q_scale = (float*)ws;
+  ws += round256((size_t)H * (nqp / kBlk) * 4);
+  float* part_o = nullptr;
+  float* part_md = nullptr;
+  if (kv_splits > 1) {
+    part_o = (float*)ws;
+    ws += round256((size_t)kv_splits * H * nqp * D * 4);
+    part_md = (float*)ws;
+  }
 
   // V cache -> per-channel e4m3 (channel-major), q -> INT8 blocks (no smoothing)
   BshdView none{nullptr, 0, 0, 0};
@@ -214,6 +256,10 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
   a.causal = 1;
   a.per_token = 1;
   a.out_bf16 = out_dtype == QATTN_OUT_BF16;
+  a.kv_splits = kv_splits;
+  a.tiles_total = (int)i8kv_key_tiles(Nq, Nk, pos0);
+  a.part_o = part_o;
+  a.part_md = part_md;
   return status_of(launch_attn_fwd(a, D, st));
 }
 

@@ -19,17 +19,22 @@ A = 0x10000000  # an aligned, never-dereferenced address (validation fails befor
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        import quantized_attention_qattn_amd._build as b
+        import importlib.util
 
+        spec = importlib.util.spec_from_file_location("qattn_build", os.path.join(os.path.dirname(LIB), "_build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     L = ct.CDLL(LIB)
     P, I, F = ct.c_void_p, ct.c_int, ct.c_float
     L.qattn_quant_qk.argtypes = [P, I64x3, P, I64x3, I, I, I, I, I, P, P, P, P, P, P]
     L.qattn_quant_v.argtypes = [P, I64x3, I, I, I, I, P, P, P]
     L.qattn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P, I64x3, I, P]
-    L.qattn_fwd_i8kv.argtypes = [P, I64x2, P, P, P, P, I, I, I, I, I, F, P, ct.c_size_t, P, I64x2, I, P]
-    L.qattn_fwd_i8kv_workspace_bytes.argtypes = [I, I, I, I]
+    L.qattn_fwd_i8kv.argtypes = [P, I64x2, P, P, P, P, I, I, I, I, I, F, I, P, ct.c_size_t, P, I64x2, I, P]
+    L.qattn_fwd_i8kv_workspace_bytes.argtypes = [I, I, I, I, I]
     L.qattn_fwd_i8kv_workspace_bytes.restype = ct.c_size_t
+    L.qattn_fwd_i8kv_kv_splits.argtypes = [I, I, I, I]
+    L.qattn_fwd_i8kv_kv_splits.restype = I
     L.qattn_p8_codes.argtypes = [P, P, ct.c_int64, P]
     L.qattn_status_string.argtypes = [I]
     L.qattn_status_string.restype = ct.c_char_p
@@ -45,7 +50,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["qattn_quant_qk", "qattn_quant_v", "qattn_fwd", "qattn_fwd_i8kv", "qattn_fwd_i8kv_workspace_bytes",
-              "qattn_status_string", "qattn_p8_codes"]:
+              "qattn_fwd_i8kv_kv_splits", "qattn_status_string", "qattn_p8_codes"]:
         assert n in names
 
 
@@ -64,10 +69,27 @@ def test_workspace_bytes(lib):
     # H*D*Nk_pad + H*D*4 + H*Nq_pad*D + H*Nq_pad/64*4, each rounded up to 256 bytes
     H, Nq, Nk, D = 32, 1024, 32768, 128
     expect = H * D * Nk + H * D * 4 + H * Nq * D + ((H * Nq // 64 * 4 + 255) // 256) * 256
-    assert lib.qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D) == expect
-    assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 64) == 2 * 64 * 64 + 512 + 2 * 64 * 64 + 256
-    assert lib.qattn_fwd_i8kv_workspace_bytes(0, 1, 1, 64) == 0
-    assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 96) == 0
+    assert lib.qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, 1) == expect
+    # split-KV adds S*H*Nq_pad*D*4 (partial O) + S*H*Nq_pad*8 (m, d')
+    assert lib.qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, 4) == expect + 4 * H * Nq * D * 4 + 4 * H * Nq * 8
+    assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 64, 1) == 2 * 64 * 64 + 512 + 2 * 64 * 64 + 256
+    assert lib.qattn_fwd_i8kv_workspace_bytes(0, 1, 1, 64, 1) == 0
+    assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 96, 1) == 0
+    assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 64, 0) == 0
+    assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 64, 65) == 0
+
+
+def test_kv_split_rule(lib):
+    # ceil(512 / (H * ceil(Nq / 256))), at least 16 key tiles per range, at most 64, at least 1
+    assert lib.qattn_fwd_i8kv_kv_splits(32, 1024, 32768, 31744) == 4  # 128 workgroups, 512 tiles
+    assert lib.qattn_fwd_i8kv_kv_splits(32, 512, 65536, 65024) == 8  # 64 workgroups, 1024 tiles
+    assert lib.qattn_fwd_i8kv_kv_splits(2, 64, 128, 64) == 1  # 2 tiles: no split
+    assert lib.qattn_fwd_i8kv_kv_splits(1, 1, 65536, 100) == 1  # 2 visible tiles
+    assert lib.qattn_fwd_i8kv_kv_splits(1, 1, 65536, 65535) == 64  # one query, 1024 tiles: capped at 64
+    assert lib.qattn_fwd_i8kv_kv_splits(1, 1, 65536, 0) == 1  # the query sees 1 key
+    assert lib.qattn_fwd_i8kv_kv_splits(8, 256, 8192, 2000) == 2  # 36 visible tiles: 2 ranges of >= 16
+    assert lib.qattn_fwd_i8kv_kv_splits(2, 64, 128, 65) == 0  # pos0 + Nq > Nk
+    assert lib.qattn_fwd_i8kv_kv_splits(0, 64, 128, 0) == 0
 
 
 def _qk(lib, **kw):
@@ -119,10 +141,11 @@ def test_fwd_validation(lib):
 def test_i8kv_validation(lib):
     qs = I64x2(128, 64)
     os_ = I64x2(128, 64)
-    need = lib.qattn_fwd_i8kv_workspace_bytes(2, 64, 128, 64)
+    need = lib.qattn_fwd_i8kv_workspace_bytes(2, 64, 128, 64, 1)
+    need2 = lib.qattn_fwd_i8kv_workspace_bytes(2, 64, 128, 64, 2)
 
-    def call(pos0=64, ws=A, wsb=need, D=64, Nq=64, Nk=128, k=A):
-        return lib.qattn_fwd_i8kv(A, qs, k, A, A, A, 2, Nq, Nk, D, pos0, 0.0, ws, wsb, A, os_, 0, None)
+    def call(pos0=64, ws=A, wsb=need, D=64, Nq=64, Nk=128, k=A, S=0):
+        return lib.qattn_fwd_i8kv(A, qs, k, A, A, A, 2, Nq, Nk, D, pos0, 0.0, S, ws, wsb, A, os_, 0, None)
 
     assert call(pos0=65) == EINVAL  # pos0 + Nq > Nk
     assert call(pos0=-1) == EINVAL
@@ -130,6 +153,9 @@ def test_i8kv_validation(lib):
     assert call(ws=A + 128) == EINVAL
     assert call(D=32) == EUNSUP
     assert call(k=None) == EINVAL
+    assert call(S=65) == EINVAL
+    assert call(S=-1) == EINVAL
+    assert call(S=2, wsb=need2 - 1) == EWS  # the partial results need room
 
 
 def test_p8_codes_validation(lib):

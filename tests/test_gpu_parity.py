@@ -275,7 +275,8 @@ def test_i8kv_small(qa):
                                     torch.from_numpy(vc).cuda(), torch.from_numpy(vts).cuda(), pos0,
                                     out_dtype=torch.float32)
         torch.cuda.synchronize()
-        ref, it = oracle.fwd_i8kv(q, kc, kts, vc, vts, pos0)
+        S = qa.qattn_fwd_i8kv_kv_splits(H, Nq, Nk, pos0)
+        ref, it = oracle.fwd_i8kv(q, kc, kts, vc, vts, pos0, kv_splits=S)
         wsh = host(ws)
         nkp, nqp = oracle.npad(Nk), oracle.npad(Nq)
         assert np.array_equal(wsh[: H * D * nkp].reshape(H, D, nkp), it["v8t"])
@@ -284,6 +285,30 @@ def test_i8kv_small(qa):
         off += (H * D * 4 + 255) // 256 * 256
         assert np.array_equal(wsh[off: off + H * nqp * D].view(np.int8).reshape(H, nqp, D), it["q8"])
         assert_close(host(out), ref, f"i8kv H={H} Nq={Nq} Nk={Nk} pos0={pos0}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_i8kv_kv_splits(qa, D):
+    """Explicit key-range counts: ranges empty for some rows (causal diagonal), for whole
+    workgroups (ranges past a query block's last visible tile) and for every row (more
+    ranges than tiles); each against the oracle's split loop and combine."""
+    rng = np.random.default_rng(62 + D)
+    for H, Nq, Nk, pos0, S in [(2, 100, 700, 600, 2), (2, 300, 1000, 17, 3), (3, 64, 200, 136, 5),
+                               (1, 1, 129, 128, 16), (2, 513, 1500, 987, 7), (2, 40, 2048, 1000, 64)]:
+        say(f"  i8kv split H={H} D={D} Nq={Nq} Nk={Nk} pos0={pos0} S={S}")
+        q = W.bf16_bits(rng.standard_normal((Nq, H, D)).astype(np.float32))
+        kc, kts = W.int8_cache(int(rng.integers(1 << 30)), 5, H, Nk, D)
+        vc, vts = W.int8_cache(int(rng.integers(1 << 30)), 6, H, Nk, D)
+        outs = []
+        for od in (torch.float32, torch.bfloat16):
+            out, _ = qa.attention_i8kv(dev_bf16(q), torch.from_numpy(kc).cuda(), torch.from_numpy(kts).cuda(),
+                                       torch.from_numpy(vc).cuda(), torch.from_numpy(vts).cuda(), pos0,
+                                       out_dtype=od, kv_splits=S)
+            outs.append(out)
+        torch.cuda.synchronize()
+        ref, _ = oracle.fwd_i8kv(q, kc, kts, vc, vts, pos0, kv_splits=S)
+        assert_close(host(outs[0]), ref, f"i8kv split H={H} Nq={Nq} Nk={Nk} pos0={pos0} S={S}")
+        assert np.array_equal(host(outs[1]), bf16_of(host(outs[0])))
 
 
 # ----------------------------------------------------------------------------------
@@ -374,8 +399,9 @@ def test_i8kv_many_heads(qa):
                                    torch.from_numpy(vc).cuda(), torch.from_numpy(vts).cuda(), pos0,
                                    out_dtype=torch.float32)
         torch.cuda.synchronize()
-        ref, _ = oracle.fwd_i8kv(q, kc, kts, vc, vts, pos0)
-        assert_close(host(out), ref, f"i8kv H={H} Nq={Nq} Nk={Nk} pos0={pos0}")
+        S = qa.qattn_fwd_i8kv_kv_splits(H, Nq, Nk, pos0)
+        ref, _ = oracle.fwd_i8kv(q, kc, kts, vc, vts, pos0, kv_splits=S)
+        assert_close(host(out), ref, f"i8kv H={H} Nq={Nq} Nk={Nk} pos0={pos0} S={S}")
 
 
 # ----------------------------------------------------------------------------------
@@ -437,9 +463,11 @@ def test_i8kv_workload_full_size(qa, name):
     heads = sorted(set([0, w.H - 1, int(rng.integers(w.H))]))
     say(f"  oracle attention on {len(rows)} rows x {len(heads)} heads")
     lam = oracle.default_lambda(D)
+    S = qa.qattn_fwd_i8kv_kv_splits(H, w.Nq, w.Nk, w.pos0)
+    say(f"  {S} key ranges")
     ref = oracle.attn(q8[:, heads], qs[:, heads], kc[None, heads], kts[None, heads], v8t[None, heads],
                       vsc[None, heads], w.Nq, w.Nk, lam, causal=True, pos_off=w.pos0, k_scale_per_token=True,
-                      rows=rows)
+                      rows=rows, kv_splits=S)
     got = host(out)[rows][:, heads][None]
     r = assert_close(got, ref, w.name)
     say(f"  max err / rms = {r:.2e}")
