@@ -124,6 +124,20 @@ size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D, int kv_split
  * (0 <= pos0, pos0 + Nq <= Nk). */
 int qattn_fwd_i8kv_kv_splits(int H, int Nq, int Nk, int pos0);
 
+/* Appends tokens to an INT8 KV cache with per-token scales, the layout qattn_fwd_i8kv
+ * reads (Strata #2092 runs its prompt attention on such a cache; the quantizer that
+ * fills it is not stated there, and the one taken is step 1's INT8 quantizer with a
+ * block of one (token, head) row).
+ *   x: bf16 [Nnew, H, D] view with strides x_str = {sn, sh} (16-byte aligned, strides
+ *      multiples of 8 elements), e.g. one projection of a packed [N, 3, H, D] tensor;
+ *   cache: int8 [H, Nmax, D] contiguous (8-byte aligned); tok_scale: f32 [H, Nmax].
+ * Token n of x goes to row pos + n of every head: a = max |x| over its D channels,
+ * tok_scale = fl32(a / 127), code = clamp(rne(fl32(x * min(fl32(127 / a), FLT_MAX))),
+ * -127, 127); a = 0 gives scale 0 and zero codes.  Other rows are not touched.
+ * 0 <= pos, pos + Nnew <= Nmax.  Call once for K and once for V. */
+int qattn_kv_append_i8(const void* x, const int64_t x_str[2], int Nnew, int H, int D, int8_t* cache,
+                       float* tok_scale, int Nmax, int pos, void* stream);
+
 /* Self-test hook: codes[i] = E4M3(2^(u[i] - 80)) computed by the fused kernel's own
  * device functions (the FP8 P code the softmax produces for the grid argument u: the
  * hardware exponential of u, then the FP8 conversion with the exact 2^80 scale).

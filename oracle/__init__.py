@@ -75,6 +75,8 @@ def lib():
             L.orc_attn_rows_part.restype = None
             L.orc_combine_rows.argtypes = [i32, P, P, P, P, i32, i32, P]
             L.orc_combine_rows.restype = None
+            L.orc_kv_append_i8.argtypes = [P, P, i32, i32, i32, P, P, i32, i32]
+            L.orc_kv_append_i8.restype = None
             L.orc_default_lambda.argtypes = [i32]
             L.orc_default_lambda.restype = f32
             L.orc_exp2_check_grid.argtypes = [_ct.c_uint32, _ct.c_uint32]
@@ -197,6 +199,21 @@ def quant_v(v: np.ndarray):
     vs = np.empty((B, H, D), dtype=np.float32)
     lib().orc_quant_v(_ptr(v), _ptr(st), B, H, N, D, _ptr(v8t), _ptr(vs))
     return v8t, vs
+
+
+def kv_append_i8(x: np.ndarray, cache: np.ndarray, tok_scale: np.ndarray, pos: int):
+    """Tokens x (bf16 bits [Nnew, H, D]) quantized into rows pos.. of copies of the int8
+    cache [H, Nmax, D] and its per-token scales [H, Nmax]; returns (cache, tok_scale)."""
+    Nnew, H, D = x.shape
+    Hc, Nmax, Dc = cache.shape
+    if (Hc, Dc) != (H, D) or tok_scale.shape != (H, Nmax) or pos < 0 or pos + Nnew > Nmax:
+        raise ValueError("kv_append_i8: shapes or position out of range")
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    cache = np.array(cache, dtype=np.int8, copy=True)
+    tok_scale = np.array(tok_scale, dtype=np.float32, copy=True)
+    st = np.array([H * D, D], dtype=np.int64)
+    lib().orc_kv_append_i8(_ptr(x), _ptr(st), Nnew, H, D, _ptr(cache), _ptr(tok_scale), Nmax, int(pos))
+    return cache, tok_scale
 
 
 def requant_v_cache(v_cache: np.ndarray, v_tok_scale: np.ndarray):

@@ -201,6 +201,38 @@ void orc_quant_i8_blocks(const uint16_t* x, const int64_t* str, const float* mea
 }
 
 /* ------------------------------------------------------------------------- */
+/* f4: appending tokens to an INT8 KV cache with per-token scales             */
+/* ------------------------------------------------------------------------- */
+/* Strata #2092 runs its prompt attention on an int8 KV cache with one fp32 scale per
+ * (head, token) and leaves the quantizer that fills it unstated.  Reading: the same
+ * symmetric INT8 quantizer as the Q/K blocks, with a block of one (token, head) row:
+ * a = max |x| over the D channels, s = fl32(a / 127), r = min(fl32(127 / a), FLT_MAX),
+ * code = clamp(rne(fl32(x * r))); a = 0 gives s = 0 and zero codes.
+ * x: bf16 [Nnew, H, D] with element strides str = {sn, sh}; token n goes to cache row
+ * pos + n: cache int8 [H, Nmax, D], tok_scale f32 [H, Nmax]; other rows are untouched. */
+void orc_kv_append_i8(const uint16_t* x, const int64_t* str, int Nnew, int H, int D, int8_t* cache,
+                      float* tok_scale, int Nmax, int pos) {
+  float* buf = (float*)malloc(sizeof(float) * D);
+  for (int n = 0; n < Nnew; ++n)
+    for (int h = 0; h < H; ++h) {
+      float a = 0.0f;
+      for (int c = 0; c < D; ++c) {
+        buf[c] = orc_bf16_to_f32(x[(int64_t)n * str[0] + (int64_t)h * str[1] + c]);
+        if (fabsf(buf[c]) > a) a = fabsf(buf[c]);
+      }
+      float s = 0.0f, rcp = 0.0f;
+      if (a > 0.0f) {
+        s = a / 127.0f;
+        rcp = fminf(127.0f / a, FLT_MAX);
+      }
+      int64_t row = (int64_t)h * Nmax + pos + n;
+      tok_scale[row] = s;
+      for (int c = 0; c < D; ++c) cache[row * D + c] = a > 0.0f ? i8_code(buf[c], rcp) : (int8_t)0;
+    }
+  free(buf);
+}
+
+/* ------------------------------------------------------------------------- */
 /* a3: V FP8 per-channel quantization (V stored transposed)                   */
 /* ------------------------------------------------------------------------- */
 /* H3 Performance Roadmap, "Measured GB10 Baseline" (V FP8 quantization row: a combined

@@ -47,6 +47,8 @@ _lib.qattn_fwd_i8kv_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.qattn_fwd_i8kv_workspace_bytes.restype = _SZ
 _lib.qattn_fwd_i8kv_kv_splits.argtypes = [_I, _I, _I, _I]
 _lib.qattn_fwd_i8kv_kv_splits.restype = _I
+_lib.qattn_kv_append_i8.argtypes = [_P, _I64x2, _I, _I, _I, _P, _P, _I, _I, _P]
+_lib.qattn_kv_append_i8.restype = _I
 _lib.qattn_p8_codes.argtypes = [_P, _P, _I64, _P]
 _lib.qattn_p8_codes.restype = _I
 _lib.qattn_status_string.argtypes = [_I]
@@ -171,6 +173,19 @@ def qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, wor
                                _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _ptr(out), _I64x2(*out.stride()[:2]), od,
                                _stream(stream)), "qattn_fwd_i8kv")
+
+
+def qattn_kv_append_i8(x, cache, tok_scale, pos: int, stream=None) -> None:
+    """x: bf16 [Nnew, H, D] view; cache: int8 [H, Nmax, D]; tok_scale: f32 [H, Nmax]."""
+    _need(x, torch.bfloat16, "x")
+    Nnew, H, D = x.shape
+    if cache.dim() != 3:
+        raise ValueError("cache: expected [H, Nmax, D]")
+    Nmax = cache.shape[1]
+    _buf(cache, torch.int8, (H, Nmax, D), "cache")
+    _buf(tok_scale, torch.float32, (H, Nmax), "tok_scale")
+    _check(_lib.qattn_kv_append_i8(_ptr(x), _I64x2(*x.stride()[:2]), Nnew, H, D, _ptr(cache), _ptr(tok_scale), Nmax,
+                                   int(pos), _stream(stream)), "qattn_kv_append_i8")
 
 
 def qattn_p8_codes(u, codes, stream=None) -> None:

@@ -94,6 +94,8 @@ struct FwdArgs {
   float* part_o;   // [kv_splits][B*H][nq_pad][D]
   float* part_md;  // [kv_splits][B*H][nq_pad][2]: m (log2 domain, -inf if none), d'
 };
+hipError_t launch_kv_append_i8(const void* x, int64_t sn, int64_t sh, int Nnew, int H, int D, int8_t* cache,
+                               float* tok_scale, int Nmax, int pos, hipStream_t st);
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st);  // both kernels when split
 hipError_t launch_p8_codes(const float* u, uint8_t* codes, int64_t n, hipStream_t st);
 

@@ -263,6 +263,19 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
   return status_of(launch_attn_fwd(a, D, st));
 }
 
+int qattn_kv_append_i8(const void* x, const int64_t x_str[2], int Nnew, int H, int D, int8_t* cache,
+                       float* tok_scale, int Nmax, int pos, void* stream) {
+  if (!cache || !tok_scale) return QATTN_EINVAL;
+  if (!bf16_view_ok(x, x_str, 2)) return QATTN_EINVAL;
+  if (!sizes_ok(1, H, Nnew) || Nmax <= 0 || Nmax > kMaxN) return QATTN_EINVAL;
+  if (D != 64 && D != 128) return QATTN_EUNSUPPORTED;
+  if (pos < 0 || (int64_t)pos + Nnew > Nmax) return QATTN_EINVAL;
+  if ((int64_t)H * Nmax * D > ((int64_t)1 << 40)) return QATTN_EINVAL;
+  if (!aligned(cache, 8) || !aligned(tok_scale, 4)) return QATTN_EINVAL;
+  return status_of(launch_kv_append_i8(x, x_str[0], x_str[1], Nnew, H, D, cache, tok_scale, Nmax, pos,
+                                       (hipStream_t)stream));
+}
+
 int qattn_p8_codes(const float* u, uint8_t* codes, int64_t n, void* stream) {
   if (!u || !codes || n <= 0) return QATTN_EINVAL;
   if (!aligned(u, 4)) return QATTN_EINVAL;

@@ -273,6 +273,61 @@ hipError_t launch_quant_i8(BshdView x, const float* mean, int B, int H, int N, i
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// KV-cache append: each (token, head) row of D channels becomes INT8 codes with its own
+// scale, by the same formula as the 64-row blocks (a = max|x|, s = a/127, code =
+// rne(x * min(127/a, FLT_MAX))).  D/8 consecutive lanes own one row (8 channels each,
+// 16-byte loads, 8-byte stores) and reduce its max with lane exchanges.
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void kv_append_i8(const uint16_t* x, int64_t sn, int64_t sh, int Nnew, int H,
+                                                         int8_t* cache, float* tok_scale, int Nmax, int pos) {
+  constexpr int CPR = D / 8;  // lanes per row (a power of two dividing 64)
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t row = t / CPR;  // n * H + h
+  const int cg = (int)(t % CPR);
+  const bool live = row < (int64_t)Nnew * H;
+  const int n = live ? (int)(row / H) : 0, h = live ? (int)(row - (int64_t)n * H) : 0;
+  float f[8];
+  float amax = 0.0f;
+  if (live) {
+    const v4i w = *(const v4i*)(x + (int64_t)n * sn + (int64_t)h * sh + cg * 8);
+    unpack_bf16x8(w, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+  // every lane of the row's group takes part (the group never straddles a wave)
+#pragma unroll
+  for (int o = CPR / 2; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, CPR));
+  if (!live) return;
+  float s = 0.0f, r = 0.0f;
+  if (amax > 0.0f) {
+    s = amax / 127.0f;
+    r = fminf(127.0f / amax, kFltMax);
+  }
+  const int64_t crow = (int64_t)h * Nmax + pos + n;
+  if (cg == 0) tok_scale[crow] = s;
+  uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float q = __builtin_rintf(f[i] * r);
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    wd[i >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (i & 3));
+  }
+  *(uint2*)(cache + crow * D + cg * 8) = make_uint2(wd[0], wd[1]);
+}
+
+hipError_t launch_kv_append_i8(const void* x, int64_t sn, int64_t sh, int Nnew, int H, int D, int8_t* cache,
+                               float* tok_scale, int Nmax, int pos, hipStream_t st) {
+  const int64_t threads = (int64_t)Nnew * H * (D / 8);
+  const int blocks = (int)((threads + kThreads - 1) / kThreads);
+  if (D == 128)
+    kv_append_i8<128><<<blocks, kThreads, 0, st>>>((const uint16_t*)x, sn, sh, Nnew, H, cache, tok_scale, Nmax, pos);
+  else
+    kv_append_i8<64><<<blocks, kThreads, 0, st>>>((const uint16_t*)x, sn, sh, Nnew, H, cache, tok_scale, Nmax, pos);
+  return hipGetLastError();
+}
+
 template <int D, bool CACHE>
 static void quant_v_impl(BshdView v, const int8_t* cache, const float* tok_scale, int B, int H, int N, int npad,
                          uint8_t* v8t, float* v_scale, hipStream_t st) {

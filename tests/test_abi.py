@@ -36,6 +36,7 @@ def lib():
     L.qattn_fwd_i8kv_kv_splits.argtypes = [I, I, I, I]
     L.qattn_fwd_i8kv_kv_splits.restype = I
     L.qattn_p8_codes.argtypes = [P, P, ct.c_int64, P]
+    L.qattn_kv_append_i8.argtypes = [P, I64x2, I, I, I, P, P, I, I, P]
     L.qattn_status_string.argtypes = [I]
     L.qattn_status_string.restype = ct.c_char_p
     return L
@@ -50,7 +51,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["qattn_quant_qk", "qattn_quant_v", "qattn_fwd", "qattn_fwd_i8kv", "qattn_fwd_i8kv_workspace_bytes",
-              "qattn_fwd_i8kv_kv_splits", "qattn_status_string", "qattn_p8_codes"]:
+              "qattn_fwd_i8kv_kv_splits", "qattn_kv_append_i8", "qattn_status_string", "qattn_p8_codes"]:
         assert n in names
 
 
@@ -156,6 +157,24 @@ def test_i8kv_validation(lib):
     assert call(S=65) == EINVAL
     assert call(S=-1) == EINVAL
     assert call(S=2, wsb=need2 - 1) == EWS  # the partial results need room
+
+
+def test_kv_append_validation(lib):
+    st = I64x2(3 * 2 * 64, 64)  # one projection of a packed [N, 3, H=2, D=64] tensor
+
+    def call(x=A, s=st, Nnew=10, H=2, D=64, cache=A, ts=A, Nmax=100, pos=0):
+        return lib.qattn_kv_append_i8(x, s, Nnew, H, D, cache, ts, Nmax, pos, None)
+
+    assert call(cache=None) == EINVAL
+    assert call(ts=None) == EINVAL
+    assert call(D=96) == EUNSUP
+    assert call(pos=91) == EINVAL  # pos + Nnew > Nmax
+    assert call(pos=-1) == EINVAL
+    assert call(x=A + 2) == EINVAL  # bf16 view not 16-byte aligned
+    assert call(s=I64x2(3 * 2 * 64, 63)) == EINVAL  # head stride not a multiple of 8 elements
+    assert call(cache=A + 4) == EINVAL  # cache not 8-byte aligned
+    assert call(Nnew=0) == EINVAL
+    assert call(Nmax=0) == EINVAL
 
 
 def test_p8_codes_validation(lib):

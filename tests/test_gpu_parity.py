@@ -311,6 +311,59 @@ def test_i8kv_kv_splits(qa, D):
         assert np.array_equal(host(outs[1]), bf16_of(host(outs[0])))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_kv_append_bit_exact(qa, D):
+    """Codes and per-token scales bit for bit against the oracle: random rows over a wide
+    range of magnitudes, zero rows, bf16 extremes, a projection-strided view, two appends
+    into one cache; rows outside each append keep their previous bytes."""
+    rng = np.random.default_rng(80 + D)
+    H, Nmax = 3, 700
+    cache = np.full((H, Nmax, D), 77, np.int8)
+    ts = np.full((H, Nmax), -1.0, np.float32)
+    dc, dts = torch.from_numpy(cache.copy()).cuda(), torch.from_numpy(ts.copy()).cuda()
+    for pos, Nnew in [(5, 300), (305, 333)]:
+        say(f"  kv append D={D} pos={pos} Nnew={Nnew}")
+        x = rng.standard_normal((Nnew, 3, H, D)).astype(np.float32) * np.exp2(rng.uniform(-30, 30, (Nnew, 1, H, 1)))
+        packed = W.bf16_bits(x)
+        packed[0, 1] = 0  # zero rows
+        packed[1, 1, 0, 0] = 0x7F7F  # largest finite bf16
+        packed[2, 1, 1, :] = 0x0001  # smallest subnormal bf16
+        dx = dev_bf16(packed)[:, 1]  # K projection of [N, 3, H, D]: strides {3 H D, D}
+        qa.qattn_kv_append_i8(dx, dc, dts, pos)
+        torch.cuda.synchronize()
+        cache, ts = oracle.kv_append_i8(packed[:, 1], cache, ts, pos)
+        assert np.array_equal(host(dc), cache)
+        assert np.array_equal(host(dts).view(np.uint32), ts.view(np.uint32))
+
+
+def test_i8kv_on_appended_cache(qa):
+    """End to end: K and V appended to the caches by the library in two chunks, then the
+    prefill over the caches; each step against the oracle's."""
+    rng = np.random.default_rng(85)
+    H, D, Nk, Nq = 4, 128, 1500, 200
+    pos0 = Nk - Nq
+    kx = W.bf16_bits(rng.standard_normal((Nk, H, D)).astype(np.float32))
+    vx = W.bf16_bits(rng.standard_normal((Nk, H, D)).astype(np.float32))
+    q = W.bf16_bits(rng.standard_normal((Nq, H, D)).astype(np.float32))
+    kc = torch.zeros((H, Nk, D), dtype=torch.int8, device="cuda")
+    vc = torch.zeros((H, Nk, D), dtype=torch.int8, device="cuda")
+    kts = torch.zeros((H, Nk), dtype=torch.float32, device="cuda")
+    vts = torch.zeros((H, Nk), dtype=torch.float32, device="cuda")
+    okc, okts = np.zeros((H, Nk, D), np.int8), np.zeros((H, Nk), np.float32)
+    ovc, ovts = okc.copy(), okts.copy()
+    for lo, hi in [(0, 1000), (1000, Nk)]:
+        qa.qattn_kv_append_i8(dev_bf16(kx[lo:hi]), kc, kts, lo)
+        qa.qattn_kv_append_i8(dev_bf16(vx[lo:hi]), vc, vts, lo)
+        okc, okts = oracle.kv_append_i8(kx[lo:hi], okc, okts, lo)
+        ovc, ovts = oracle.kv_append_i8(vx[lo:hi], ovc, ovts, lo)
+    out, _ = qa.attention_i8kv(dev_bf16(q), kc, kts, vc, vts, pos0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(kc), okc) and np.array_equal(host(vts), ovts)
+    S = qa.qattn_fwd_i8kv_kv_splits(H, Nq, Nk, pos0)
+    ref, _ = oracle.fwd_i8kv(q, okc, okts, ovc, ovts, pos0, kv_splits=S)
+    assert_close(host(out), ref, "i8kv on appended cache")
+
+
 # ----------------------------------------------------------------------------------
 # many heads (grids of several hundred 256-row workgroups, every XCD busy)
 # ----------------------------------------------------------------------------------
@@ -413,13 +466,14 @@ def _sample_rows(Nq, rng, nblk=3):
     return np.array(rows)
 
 
-@pytest.mark.parametrize("name", ["dense_b1_h16_n4096_d128", "video_dit_b1_h24_n37810_d128"])
+@pytest.mark.parametrize("name", ["dense_b1_h16_n4096_d128", "video_dit_b1_h24_n37810_d128",
+                                  "video_dit_b1_h24_n74000_d128", "causal_b1_h24_n37810_d128"])
 def test_dense_workload_full_size(qa, name):
     w = W.BY_NAME[name]
     say(f"full-size {w.name}: generating inputs")
     q, k, v = W.dense_inputs(w)
     dq, dk, dv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
-    out, inter = qa.attention(dq, dk, dv, out_dtype=torch.float32)
+    out, inter = qa.attention(dq, dk, dv, causal=w.causal, out_dtype=torch.float32)
     torch.cuda.synchronize()
     say("  oracle quantizers")
     q8, qs, k8, ks, mean = oracle.quant_qk(q, k)
@@ -434,11 +488,12 @@ def test_dense_workload_full_size(qa, name):
     say(f"  oracle attention on {len(rows)} rows x {len(heads)} heads")
     lam = oracle.default_lambda(w.D)
     sel = (slice(None), heads)
-    ref = oracle.attn(q8[sel], qs[sel], k8[sel], ks[sel], v8t[sel], vs[sel], w.Nq, w.Nk, lam, rows=rows)
+    ref = oracle.attn(q8[sel], qs[sel], k8[sel], ks[sel], v8t[sel], vs[sel], w.Nq, w.Nk, lam, causal=w.causal,
+                      rows=rows)
     got = host(out)[:, rows][:, :, heads]
     r = assert_close(got, ref, w.name)
     say(f"  max err / rms = {r:.2e}")
-    out16, _ = qa.attention(dq, dk, dv, out_dtype=torch.bfloat16)
+    out16, _ = qa.attention(dq, dk, dv, causal=w.causal, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert np.array_equal(host(out16)[:, rows][:, :, heads], bf16_of(host(out)[:, rows][:, :, heads]))
 

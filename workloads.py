@@ -58,8 +58,13 @@ PREFILL32K = Workload("prefill_i8kv_h32_d128_q1024_ctx32768", "i8kv", H=32, D=12
 PREFILL64K = Workload("prefill_i8kv_h32_d128_q512_ctx65536", "i8kv", H=32, D=128, Nq=512, Nk=65536, causal=True,
                       pos0=65024, seed=SEED_BASE + 4)
 VIDEO37810 = Workload("video_dit_b1_h24_n37810_d128", "dense", H=24, D=128, Nq=37810, Nk=37810, seed=SEED_BASE + 5)
+# the longer video baseline the pages name ("74K tokens"; count taken literally, ragged last tile)
+VIDEO74000 = Workload("video_dit_b1_h24_n74000_d128", "dense", H=24, D=128, Nq=74000, Nk=74000, seed=SEED_BASE + 6)
+# causal dense self-attention at the video size (ops counted on the visible pairs)
+CAUSAL37810 = Workload("causal_b1_h24_n37810_d128", "dense", H=24, D=128, Nq=37810, Nk=37810, causal=True,
+                       seed=SEED_BASE + 7)
 
-ALL = [TINY, DENSE4096, PREFILL32K, PREFILL64K, VIDEO37810]
+ALL = [TINY, DENSE4096, PREFILL32K, PREFILL64K, VIDEO37810, VIDEO74000, CAUSAL37810]
 BY_NAME = {w.name: w for w in ALL}
 
 
