@@ -284,7 +284,9 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   // range of one (b, h) are neighbours, so an XCD's L2 serves all their query blocks
   const int work = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, gridDim.x));
   const int rest = __builtin_amdgcn_readfirstlane(work / nqb);
-  const int qblk = work - rest * nqb;
+  // causal: the last query blocks see the most keys, so they are dispatched first and the
+  // final wave of workgroups is the light one
+  const int qblk = CAUSAL ? nqb - 1 - (work - rest * nqb) : work - rest * nqb;
   const int bh = __builtin_amdgcn_readfirstlane(rest / a.kv_splits);
   const int split = rest - bh * a.kv_splits;
   const int q0 = qblk * BM;
