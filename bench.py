@@ -157,11 +157,11 @@ def main():
 
         def step(record):
             qa.qattn_quant_qk(dq, dk, t_qk["q8"], t_qk["q_scale"], t_qk["k8"], t_qk["k_scale"], t_qk["k_mean"])
-            qa.qattn_quant_v(dv, t_v["v8t"], t_v["v_scale"])
+            qa.qattn_quant_v(dv, t_v["v8t"], t_v["v_scale"], t_v["vbf"])
             if record:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            qa.qattn_fwd(t_qk["q8"], t_qk["q_scale"], t_qk["k8"], t_qk["k_scale"], t_v["v8t"], t_v["v_scale"], w.Nq,
+            qa.qattn_fwd(t_qk["q8"], t_qk["q_scale"], t_qk["k8"], t_qk["k_scale"], t_v["vbf"], t_v["v_scale"], w.Nq,
                          w.Nk, out, 0.0, w.causal)
             if record:
                 e1.record(stream)

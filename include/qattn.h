@@ -18,7 +18,7 @@
  *   - Strides are in elements; the innermost (D) stride is always 1.
  *   - D (head dimension) must be 64 or 128 (QATTN_EUNSUPPORTED otherwise).
  *   - bf16 inputs: base 16-byte aligned, strides multiples of 8 elements.
- *     Code buffers (q8, k8, v8t) and the workspace: 256-byte aligned.
+ *     Code buffers (q8, k8, v8t, vbf) and the workspace: 256-byte aligned.
  *     Scale buffers: 4-byte aligned.  Outputs: base and strides aligned to 4 elements.
  *   - N_pad = ceil(N / 64) * 64.  Code layouts are zero-padded to N_pad rows/columns.
  *   - Results are bitwise deterministic run to run (no atomics).
@@ -69,21 +69,25 @@ int qattn_quant_qk(const void* q, const int64_t q_str[3], const void* k, const i
  * Per (b, h, channel): a = max|v| over the Nk tokens, scale = fl32(a/448), code =
  * E4M3(fl32(v * min(fl32(448/a), FLT_MAX))) rounded to nearest even, saturated at 448,
  * sign kept; a = 0 gives scale 0 and 0x00 codes.  v8t and v_scale are used as scratch
- * during the call. */
+ * during the call.
+ *   vbf (optional, may be NULL): bf16 [B, H, D, Nk_pad] (256-byte aligned), the exact
+ *   values of the v8t codes (every e4m3 value is a bf16 value; padding tokens 0) -- the
+ *   form of V the fused loop reads. */
 int qattn_quant_v(const void* v, const int64_t v_str[3], int B, int H, int Nk, int D, uint8_t* v8t,
-                  float* v_scale, void* stream);
+                  float* v_scale, uint16_t* vbf, void* stream);
 
 /* Steps 3-5 -- fused INT8 QK, online softmax with FP8 P, PV and epilogue ("Sage2 SM89
  * Temporal Pair Experiment", "Candidate": per 64-key tile QK -> update m, d, O ->
  * accumulate d -> P to 8 bit -> PV), on the outputs of steps 1-2 (same layouts).
  * PV sums the exact products of the e4m3 values of P and V in fp32 (no truncation of
- * small products).
+ * small products).  V enters as vbf, the bf16 values of the step-2 codes (qattn_quant_v's
+ * vbf output), so the loop reads V tiles that its matrix instructions take as they are.
  *   scale_log2: softmax scale times log2(e); <= 0 selects fl32(fl32(1/sqrt(D)) * log2e).
  *   causal: key j visible to query i iff j <= i + (Nk - Nq) (bottom-right aligned); a
  *           query with no visible key outputs zeros.
  *   out: [B, Nq, H, D] view with strides out_str, dtype out_dtype (token-major NHD).
  * Output = fl32(O * s_v / d') with fp32 accumulation; bf16 output is its RNE rounding. */
-int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale, const uint8_t* v8t,
+int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale, const uint16_t* vbf,
               const float* v_scale, int B, int H, int Nq, int Nk, int D, float scale_log2, int causal, void* out,
               const int64_t out_str[3], int out_dtype, void* stream);
 
@@ -95,8 +99,8 @@ int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const fl
  *      (one scale per head and token: value = code * scale).
  *   workspace: >= qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D) bytes, 256-byte aligned;
  *      receives the per-channel e4m3 requantization of V (fl32(code * scale) quantized
- *      as in step 2 over all Nk tokens) and the INT8 blocks of q (as in step 1, no
- *      smoothing).
+ *      as in step 2 over all Nk tokens; its codes and their bf16 values) and the INT8
+ *      blocks of q (as in step 1, no smoothing).
  *   kv_splits: split-KV for few queries over a long context.  The key tiles
  *      [0, T), T = ceil(min(Nk, pos0 + Nq) / 64), are cut into kv_splits contiguous ranges
  *      [s T / S, (s + 1) T / S); each range runs the loop above on its own (from
@@ -113,7 +117,8 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
 
 /* Workspace size for qattn_fwd_i8kv with kv_splits key ranges (1 .. 64; resolve 0 with
  * qattn_fwd_i8kv_kv_splits first): H*D*Nk_pad (e4m3 V) + H*D*4 (V scales) + H*Nq_pad*D
- * (q codes) + H*Nq_pad/64*4 (q scales), and for kv_splits > 1 the partial results
+ * (q codes) + H*Nq_pad/64*4 (q scales) + H*D*Nk_pad*2 (bf16 values of the V codes), and
+ * for kv_splits > 1 the partial results
  * kv_splits*H*Nq_pad*D*4 (O) + kv_splits*H*Nq_pad*8 (m, d'), each section rounded up to
  * 256 bytes.  Returns 0 for invalid sizes. */
 size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D, int kv_splits);

@@ -12,6 +12,7 @@ Layouts (N_pad = ceil(N / 64) * 64):
   q8, k8    int8 [B, H, N_pad, D];  q_scale, k_scale f32 [B, H, N_pad / 64]
   k_mean    f32 [B, H, D]
   v8t       uint8 (e4m3fn codes) [B, H, D, N_pad];  v_scale f32 [B, H, D]
+  vbf       bf16 [B, H, D, N_pad]: the values of the v8t codes, the V operand of qattn_fwd
   out       bf16 or f32 [B, Nq, H, D]
 """
 from __future__ import annotations
@@ -37,7 +38,7 @@ _I64x3 = _ct.c_int64 * 3
 _I64x2 = _ct.c_int64 * 2
 _lib.qattn_quant_qk.argtypes = [_P, _I64x3, _P, _I64x3, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
 _lib.qattn_quant_qk.restype = _I
-_lib.qattn_quant_v.argtypes = [_P, _I64x3, _I, _I, _I, _I, _P, _P, _P]
+_lib.qattn_quant_v.argtypes = [_P, _I64x3, _I, _I, _I, _I, _P, _P, _P, _P]
 _lib.qattn_quant_v.restype = _I
 _lib.qattn_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I64x3, _I, _P]
 _lib.qattn_fwd.restype = _I
@@ -120,28 +121,30 @@ def qattn_quant_qk(q, k, q8, q_scale, k8, k_scale, k_mean, stream=None) -> None:
            "qattn_quant_qk")
 
 
-def qattn_quant_v(v, v8t, v_scale, stream=None) -> None:
+def qattn_quant_v(v, v8t, v_scale, vbf=None, stream=None) -> None:
     _need(v, torch.bfloat16, "v")
     B, Nk, H, D = v.shape
     _buf(v8t, torch.uint8, (B, H, D, npad(Nk)), "v8t")
     _buf(v_scale, torch.float32, (B, H, D), "v_scale")
+    if vbf is not None:
+        _buf(vbf, torch.bfloat16, (B, H, D, npad(Nk)), "vbf")
     _check(_lib.qattn_quant_v(_ptr(v), _I64x3(*v.stride()[:3]), B, H, Nk, D, _ptr(v8t), _ptr(v_scale),
-                              _stream(stream)), "qattn_quant_v")
+                              None if vbf is None else _ptr(vbf), _stream(stream)), "qattn_quant_v")
 
 
-def qattn_fwd(q8, q_scale, k8, k_scale, v8t, v_scale, Nq: int, Nk: int, out, scale_log2: float = 0.0,
+def qattn_fwd(q8, q_scale, k8, k_scale, vbf, v_scale, Nq: int, Nk: int, out, scale_log2: float = 0.0,
               causal: bool = False, stream=None) -> None:
     B, H, _, D = q8.shape
     _buf(q8, torch.int8, (B, H, npad(Nq), D), "q8")
     _buf(q_scale, torch.float32, (B, H, npad(Nq) // BLOCK), "q_scale")
     _buf(k8, torch.int8, (B, H, npad(Nk), D), "k8")
     _buf(k_scale, torch.float32, (B, H, npad(Nk) // BLOCK), "k_scale")
-    _buf(v8t, torch.uint8, (B, H, D, npad(Nk)), "v8t")
+    _buf(vbf, torch.bfloat16, (B, H, D, npad(Nk)), "vbf")
     _buf(v_scale, torch.float32, (B, H, D), "v_scale")
     if not out.is_cuda or tuple(out.shape) != (B, Nq, H, D) or out.stride(3) != 1:
         raise ValueError(f"out: expected a CUDA [B, Nq, H, D] = {(B, Nq, H, D)} view with unit channel stride")
     od = QATTN_OUT_BF16 if out.dtype == torch.bfloat16 else QATTN_OUT_F32 if out.dtype == torch.float32 else -1
-    _check(_lib.qattn_fwd(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v8t), _ptr(v_scale), B, H, Nq, Nk,
+    _check(_lib.qattn_fwd(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(vbf), _ptr(v_scale), B, H, Nq, Nk,
                           D, float(scale_log2), 1 if causal else 0, _ptr(out), _I64x3(*out.stride()[:3]), od,
                           _stream(stream)), "qattn_fwd")
 
@@ -211,7 +214,8 @@ def alloc_qk(B: int, H: int, Nq: int, Nk: int, D: int, device="cuda"):
 
 def alloc_v(B: int, H: int, Nk: int, D: int, device="cuda"):
     return dict(v8t=torch.empty((B, H, D, npad(Nk)), dtype=torch.uint8, device=device),
-                v_scale=torch.empty((B, H, D), dtype=torch.float32, device=device))
+                v_scale=torch.empty((B, H, D), dtype=torch.float32, device=device),
+                vbf=torch.empty((B, H, D, npad(Nk)), dtype=torch.bfloat16, device=device))
 
 
 def quant_qk(q, k, stream=None):
@@ -224,7 +228,7 @@ def quant_qk(q, k, stream=None):
 def quant_v(v, stream=None):
     B, Nk, H, D = v.shape
     t = alloc_v(B, H, Nk, D, v.device)
-    qattn_quant_v(v, t["v8t"], t["v_scale"], stream)
+    qattn_quant_v(v, t["v8t"], t["v_scale"], t["vbf"], stream)
     return t
 
 
@@ -234,7 +238,7 @@ def attention(q, k, v, causal: bool = False, scale_log2: float = 0.0, out_dtype=
     qk = quant_qk(q, k, stream)
     vv = quant_v(v, stream)
     out = torch.empty((B, Nq, H, D), dtype=out_dtype, device=q.device)
-    qattn_fwd(qk["q8"], qk["q_scale"], qk["k8"], qk["k_scale"], vv["v8t"], vv["v_scale"], Nq, k.shape[1], out,
+    qattn_fwd(qk["q8"], qk["q_scale"], qk["k8"], qk["k_scale"], vv["vbf"], vv["v_scale"], Nq, k.shape[1], out,
               scale_log2, causal, stream)
     return out, {**qk, **vv}
 

@@ -25,22 +25,19 @@
 //     of gfx950 was not used here: it truncates each product to 13 bits below the
 //     largest product of its group of 8, which moves outputs by up to ~1e-3 of their
 //     RMS and breaks the accuracy contract;
-//   * K tiles (INT8) and V^T tiles (FP8 codes) are loaded straight into LDS; each group-0
-//     wave widens the V^T chunks its own loads brought in to bf16 once, at the end of
-//     its VALU phase (where it would otherwise wait for group 1), so the MFMA phases
-//     read bf16 V^T fragments directly;
+//   * K tiles (INT8) and V^T tiles (the bf16 values of the V codes, written by the V
+//     quantizer beside the codes) are loaded straight into LDS, so the MFMA phases read
+//     the PV operand as it is;
 //   * O^T (D x 32 queries per wave) lives in D/32 accumulators of 16 fp32 per lane;
 //   * workgroups are mapped so each XCD walks one contiguous range of (b, h, query block)
 //     and keeps the K/V it streams in its own L2.
 //
 // Tile pipeline (tick k = the interval between two workgroup barriers; group 0 runs
 // phase k of its sequence M0 V0 M1 V1 ..., group 1 phase k - 1):
-//   slot j = {K tile j, V^T codes of tile j - 1} sits in buffer j % 3.  Group 0 issues
-//   the loads of slot j at the start of its MFMA phase j - 2 (tick 2j - 4), waits for
-//   them at the end of its VALU phase j - 1 (tick 2j - 1) and there widens the V^T
-//   codes into the bf16 buffer (j - 1) & 1.  The MFMA phases j read slot j and that
-//   bf16 tile at ticks 2j (group 0) and 2j + 1 (group 1); the slot buffer is reloaded
-//   at tick 2j + 2 and the bf16 buffer rewritten at tick 2j + 3.
+//   slot j = {K tile j, bf16 V^T of tile j - 1} sits in buffer j % 3.  Group 0 issues
+//   the loads of slot j at the start of its VALU phase j - 2 (tick 2j - 3) and waits for
+//   them at the end of its VALU phase j - 1 (tick 2j - 1).  The MFMA phases j read slot
+//   j at ticks 2j (group 0) and 2j + 1 (group 1); the buffer is reloaded at tick 2j + 3.
 #include <climits>
 #include <type_traits>
 
@@ -266,11 +263,11 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NS = D / 32;        // QK k-steps = O accumulator blocks
   constexpr int KCH = D / 16;       // 16-byte chunks per K row
-  constexpr int PT = D / 64;        // 16-byte chunks per loading thread per tile (K and V each)
+  constexpr int PT = D / 64;        // 16-byte chunks per loading thread per K tile
+  constexpr int PTV = D / 32;       // 16-byte chunks per loading thread per bf16 V^T tile
   constexpr int QB = BM / kBlk;     // 64-row Q scale blocks per workgroup
   __shared__ __align__(16) uint8_t sK[NBUF][BN * D];   // K codes, swizzled for the QK reads
-  __shared__ __align__(16) uint8_t sV[NBUF][D * BN];   // V^T codes, linear (loaded and widened by group 0)
-  __shared__ __align__(16) uint8_t sVb[2][D * BN * 2];  // V^T bf16 of tile j in buffer j & 1, swizzled
+  __shared__ __align__(16) uint8_t sVb[NBUF][D * BN * 2];  // bf16 V^T of each slot, swizzled
   __shared__ __align__(16) float sC[2][QB][BN];     // PER_TOKEN: c_j per (buffer, query block, key)
   __shared__ __align__(16) float sKs[NBUF][BN];     // PER_TOKEN: raw K scales of each slot
 
@@ -331,33 +328,40 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   wtiles = __builtin_amdgcn_readfirstlane(max(0, min(wtiles, t_end) - t0));
 
   // ---- staging: global -> LDS directly (buffer loads with the LDS destination) ----
-  // Each group-0 wave fills PT 1 KiB segments of the K tile and of the V^T code tile;
+  // Each group-0 wave fills PT 1 KiB segments of the K tile and PTV of the bf16 V^T tile;
   // lane l of a segment writes LDS slot 64 seg + l (16 bytes), so each lane fetches the
   // global chunk that the swizzled layout keeps in that slot.
   // Buffer resources are per (b, h) with 32-bit offsets; rows past the end of the
   // resource (a KV cache whose length is not a multiple of 64) read as zeros.
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(a.k8 + bh * a.k8_bh), (short)0, a.k_rows * D, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(a.v8t + bh * a.v8t_bh), (short)0, (int)(D * a.ldv), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(a.vbf + bh * a.vbf_bh),
+                                                                       (short)0, (int)(2 * D * a.ldv), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)uniform_ptr(a.k_scale + bh * a.ks_bh), (short)0, PER_TOKEN ? a.Nk * 4 : 0, kRsrcWord3);
-  int koff[PT], voff[PT];
+  int koff[PT], voff[PTV];
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int slot = 64 * ((wave & 3) * PT + i) + lane;
     const int row = slot / KCH, pc = slot % KCH;
     koff[i] = row * D + 16 * (pc ^ kswz<D>(row));
-    voff[i] = (slot >> 2) * (int)a.ldv + 16 * (slot & 3);
   }
-  // Slot t: K tile t and its raw per-token K scales (t < ntiles), and the V^T codes of
+  // bf16 V^T rows are 128 bytes (8 slots): slot L holds chunk (L & 7) ^ vbswz(row) of
+  // channel row L >> 3, i.e. keys 8 q .. 8 q + 7 of that channel
+#pragma unroll
+  for (int i = 0; i < PTV; ++i) {
+    const int slot = 64 * ((wave & 3) * PTV + i) + lane;
+    const int row = slot >> 3, q = (slot & 7) ^ vbswz(slot >> 3);
+    voff[i] = row * (int)(2 * a.ldv) + 16 * q;
+  }
+  // Slot t: K tile t and its raw per-token K scales (t < ntiles), and the bf16 V^T of
   // tile t - 1 (t >= 1), into buffer buf = t % NBUF.  Every group-0 wave loads all 64
   // raw scales of the tile itself (the waves write identical bytes), so that its own
   // wait makes them visible to it.  All slot traffic goes through the direct-to-LDS
   // loads: a compiler-visible load whose value is used while tile loads are in flight
   // would make the compiler wait for all of them.
   // LDS byte addresses of the buffers, formed once (wave-uniform)
-  const uint32_t ldsK0 = lds_addr(&sK[0][0]), ldsV0 = lds_addr(&sV[0][0]), ldsKs0 = lds_addr(&sKs[0][0]);
+  const uint32_t ldsK0 = lds_addr(&sK[0][0]), ldsV0 = lds_addr(&sVb[0][0]), ldsKs0 = lds_addr(&sKs[0][0]);
   auto stage = [&](int t, int buf) {
     if (PER_TOKEN && t < ntiles) dma_4B(srs, ldsKs0 + buf * (4 * BN), 4 * lane, 4 * (t0 + t) * BN);
 #pragma unroll
@@ -365,40 +369,24 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
       // wave-uniform; readfirstlane tells the compiler so (the asm needs an SGPR)
       const uint32_t seg = __builtin_amdgcn_readfirstlane(1024u * ((wave & 3) * PT + i));
       if (t < ntiles) dma_16B(krs, ldsK0 + buf * (BN * D) + seg, koff[i], (t0 + t) * BN * D);
-      if (t > 0) dma_16B(vrs, ldsV0 + buf * (D * BN) + seg, voff[i], (t0 + t - 1) * BN);
+    }
+#pragma unroll
+    for (int i = 0; i < PTV; ++i) {
+      const uint32_t seg = __builtin_amdgcn_readfirstlane(1024u * ((wave & 3) * PTV + i));
+      if (t > 0) dma_16B(vrs, ldsV0 + buf * (2 * D * BN) + seg, voff[i], (t0 + t - 1) * BN * 2);
     }
   };
   // wait until at most the loads of slot t are in flight (t > ntiles: none)
+  static_assert(PT + PTV + 1 < 64, "vmcnt immediate");
   auto wait_all_but = [&](int t) {
     if (t > ntiles)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    else if (t == ntiles)  // last slot: V^T codes only
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PT));
+    else if (t == ntiles)  // last slot: V^T only
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PTV));
     else if (t > 0)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PT + (PER_TOKEN ? 1 : 0)));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PT + PTV + (PER_TOKEN ? 1 : 0)));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(PT + (PER_TOKEN ? 1 : 0)));
-  };
-  // Widen the V^T codes this wave loaded into buffer buf (tile v) to bf16: lane l of
-  // segment seg holds code chunk 64 seg + l = (channel row r, keys 16 kc .. 16 kc + 15),
-  // written as bf16 chunks 2 kc and 2 kc + 1 of row r.
-  // (load at the start of the VALU phase, widen and store at its end)
-  auto widen_load = [&](int buf, v4i* c) {
-#pragma unroll
-    for (int i = 0; i < PT; ++i) c[i] = *(const v4i*)&sV[buf][16 * (64 * ((wave & 3) * PT + i) + lane)];
-  };
-  auto widen_store = [&](int v, const v4i* c) {
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int slot = 64 * ((wave & 3) * PT + i) + lane;
-      const int r = slot >> 2, kc = slot & 3;
-      uint32_t w[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) fp8x4_to_bf16(c[i][e], w[2 * e], w[2 * e + 1]);
-      uint8_t* rowp = &sVb[v & 1][r * (2 * BN)];
-      *(v4i*)(rowp + 16 * ((2 * kc) ^ vbswz(r))) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-      *(v4i*)(rowp + 16 * ((2 * kc + 1) ^ vbswz(r))) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-    }
   };
   auto scale_store = [&](int t, int buf) {  // c of slot t (buffer buf), after its wait
     if (PER_TOKEN) sC[t & 1][gtid >> 6][gtid & (BN - 1)] = (sq_mine * sKs[buf][gtid & (BN - 1)]) * a.lambda;
@@ -415,10 +403,10 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) pb[j] = 0u;
 
-  // the first MFMA phase reads bf16 buffer 1 with P = 0: it must hold finite values
-  // (uninitialized LDS may hold NaN patterns)
-  if (16 * tid < 2 * D * BN) *(v4i*)&sVb[1][16 * tid] = v4i{0, 0, 0, 0};
-  if (D * BN > 8 * NT) *(v4i*)&sVb[1][16 * (tid + NT)] = v4i{0, 0, 0, 0};
+  // the first MFMA phase reads the V^T of slot 0 (no tile: never loaded) with P = 0: it
+  // must hold finite values (uninitialized LDS may hold NaN patterns)
+  if (16 * tid < 2 * D * BN) *(v4i*)&sVb[0][16 * tid] = v4i{0, 0, 0, 0};
+  if (D * BN > 8 * NT) *(v4i*)&sVb[0][16 * (tid + NT)] = v4i{0, 0, 0, 0};
   // Q fragment and scales are in registers before any tile load: otherwise the
   // compiler's waits for them, placed inside the loop, would also wait for the tile
   // loads in flight
@@ -442,7 +430,6 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     // ---- MFMA phase i: S = K_i . Q^T and O^T += V_{i-1}^T . P_{i-1}^T ----
     const int buf1 = buf == NBUF - 1 ? 0 : buf + 1;
     const int buf2 = buf1 == NBUF - 1 ? 0 : buf1 + 1;
-    if (grp == 0 && i + 2 <= ntiles) stage(i + 2, buf2);
     // The MFMA phase has one branch-free form: the first one runs PV on a zeroed V^T
     // buffer with P = 0, the last one computes a QK that nobody reads, and a wave whose
     // rows see no key of the tile has P = 0 (separate forms would make the compiler copy
@@ -452,7 +439,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     // consumed (register budget).  The PV MFMAs run chunk-major, so consecutive MFMAs
     // accumulate into different O blocks.
     const uint8_t* tK = sK[buf];
-    const uint8_t* tV = sVb[(i + 1) & 1];  // bf16 V^T of tile i - 1
+    const uint8_t* tV = sVb[buf];  // bf16 V^T of tile i - 1
     // lane (channel row, half hh) reads the bf16 V^T of keys 32 hh + 8 c .. + 7 of its row
     auto read_v = [&](int s, int c) {
       const int vrow = 32 * s + l32;
@@ -503,13 +490,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     phase_barrier();
 
     // ---- VALU phase i: online softmax of tile i ----
-    // group 0: slot i + 1 landed long ago (issued three ticks back); its V^T codes are
-    // read now and widened after the softmax, so the read latency is hidden
-    v4i wcodes[PT];
-    if (grp == 0 && i < ntiles) {
-      wait_all_but(i + 2);
-      widen_load(buf1, wcodes);
-    }
+    if (grp == 0 && i + 2 <= ntiles) stage(i + 2, buf2);
     // per-tile K scale of this tile (loaded during the previous VALU phase) and of the
     // next one: uniform addresses read through the constant address space, i.e. scalar
     // loads, issued a phase ahead so that their latency is never waited for
@@ -543,8 +524,10 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) pb[j] = 0u;  // no contribution from this tile
     }
+    // group 0: slot i + 1 (issued three ticks back) must have landed before the MFMA
+    // phases i + 1 read it; its raw K scales give the c of tile i + 1
     if (grp == 0 && i < ntiles) {
-      widen_store(i, wcodes);  // V^T of tile i, read by the MFMA phases i + 1
+      wait_all_but(i + 2);
       if (i + 1 < ntiles) scale_store(i + 1, buf1);
     }
     phase_barrier();

@@ -70,17 +70,17 @@ hipError_t launch_quant_i8(BshdView x, const float* mean, int B, int H, int N, i
                            float* scales, hipStream_t st);
 // V: bf16 view (cache == nullptr) or int8 cache [H, N, D] with per-token scales (B must be 1)
 hipError_t launch_quant_v(BshdView v, const int8_t* cache, const float* tok_scale, int B, int H, int N, int D,
-                          int npad, uint8_t* v8t, float* v_scale, hipStream_t st);
+                          int npad, uint8_t* v8t, float* v_scale, uint16_t* vbf, hipStream_t st);
 
 struct FwdArgs {
   const int8_t* q8;
   const float* q_scale;
   const int8_t* k8;
   const float* k_scale;
-  const uint8_t* v8t;
+  const uint16_t* vbf;  // bf16 values of the V^T e4m3 codes [B*H][D][ldv]
   const float* v_scale;
   void* out;
-  int64_t q8_bh, qs_bh, k8_bh, ks_bh, v8t_bh, ldv;  // per-(b,h) element strides
+  int64_t q8_bh, qs_bh, k8_bh, ks_bh, vbf_bh, ldv;  // per-(b,h) element strides
   int64_t out_sb, out_sn, out_sh;
   int B, H, Nq, Nk, nq_pad, k_rows;
   float lambda;

@@ -86,14 +86,15 @@ int qattn_quant_qk(const void* q, const int64_t q_str[3], const void* k, const i
 }
 
 int qattn_quant_v(const void* v, const int64_t v_str[3], int B, int H, int Nk, int D, uint8_t* v8t, float* v_scale,
-                  void* stream) {
+                  uint16_t* vbf, void* stream) {
   if (!v8t || !v_scale) return QATTN_EINVAL;
+  if (vbf && !aligned(vbf, 256)) return QATTN_EINVAL;
   if (!bf16_view_ok(v, v_str, 3)) return QATTN_EINVAL;
   if (!sizes_ok(B, H, Nk)) return QATTN_EINVAL;
   if (D != 64 && D != 128) return QATTN_EUNSUPPORTED;
   if (!aligned(v8t, 256) || !aligned(v_scale, 4)) return QATTN_EINVAL;
   BshdView vv{v, v_str[0], v_str[1], v_str[2]};
-  return status_of(launch_quant_v(vv, nullptr, nullptr, B, H, Nk, D, (int)npad64(Nk), v8t, v_scale,
+  return status_of(launch_quant_v(vv, nullptr, nullptr, B, H, Nk, D, (int)npad64(Nk), v8t, v_scale, vbf,
                                   (hipStream_t)stream));
 }
 
@@ -107,13 +108,13 @@ static bool out_ok(const void* out, const int64_t* str, int n, int out_dtype) {
   return true;
 }
 
-int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale, const uint8_t* v8t,
+int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale, const uint16_t* vbf,
               const float* v_scale, int B, int H, int Nq, int Nk, int D, float scale_log2, int causal, void* out,
               const int64_t out_str[3], int out_dtype, void* stream) {
-  if (!q8 || !q_scale || !k8 || !k_scale || !v8t || !v_scale) return QATTN_EINVAL;
+  if (!q8 || !q_scale || !k8 || !k_scale || !vbf || !v_scale) return QATTN_EINVAL;
   if (!sizes_ok(B, H, Nq) || !sizes_ok(B, H, Nk)) return QATTN_EINVAL;
   if (D != 64 && D != 128) return QATTN_EUNSUPPORTED;
-  if (!aligned(q8, 256) || !aligned(k8, 256) || !aligned(v8t, 256)) return QATTN_EINVAL;
+  if (!aligned(q8, 256) || !aligned(k8, 256) || !aligned(vbf, 256)) return QATTN_EINVAL;
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4)) return QATTN_EINVAL;
   if (!out_ok(out, out_str, 3, out_dtype)) return QATTN_EINVAL;
   if (isnan(scale_log2) || isinf(scale_log2)) return QATTN_EINVAL;
@@ -125,14 +126,14 @@ int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const fl
   a.q_scale = q_scale;
   a.k8 = k8;
   a.k_scale = k_scale;
-  a.v8t = v8t;
+  a.vbf = vbf;
   a.v_scale = v_scale;
   a.out = out;
   a.q8_bh = nqp * D;
   a.qs_bh = nqp / kBlk;
   a.k8_bh = nkp * D;
   a.ks_bh = nkp / kBlk;
-  a.v8t_bh = (int64_t)D * nkp;
+  a.vbf_bh = (int64_t)D * nkp;
   a.ldv = nkp;
   a.out_sb = out_str[0];
   a.out_sn = out_str[1];
@@ -175,7 +176,7 @@ size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D, int kv_split
   if (kv_splits < 1 || kv_splits > kMaxKvSplits) return 0;
   const size_t nkp = (size_t)npad64(Nk), nqp = (size_t)npad64(Nq);
   size_t bytes = round256((size_t)H * D * nkp) + round256((size_t)H * D * 4) + round256((size_t)H * nqp * D) +
-                 round256((size_t)H * (nqp / kBlk) * 4);
+                 round256((size_t)H * (nqp / kBlk) * 4) + round256((size_t)H * D * nkp * 2);
   if (kv_splits > 1)
     bytes += round256((size_t)kv_splits * H * nqp * D * 4) + round256((size_t)kv_splits * H * nqp * 2 * 4);
   return bytes;
@@ -212,6 +213,8 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
   ws += round256((size_t)H * nqp * D);
   float* q_scale = (float*)ws;
   ws += round256((size_t)H * (nqp / kBlk) * 4);
+  uint16_t* vbf = (uint16_t*)ws;
+  ws += round256((size_t)H * D * nkp * 2);
   float* part_o = nullptr;
   float* part_md = nullptr;
   if (kv_splits > 1) {
@@ -222,7 +225,7 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
 
   // V cache -> per-channel e4m3 (channel-major), q -> INT8 blocks (no smoothing)
   BshdView none{nullptr, 0, 0, 0};
-  hipError_t e = launch_quant_v(none, v_cache, v_tok_scale, 1, H, Nk, D, (int)nkp, v8t, v_scale, st);
+  hipError_t e = launch_quant_v(none, v_cache, v_tok_scale, 1, H, Nk, D, (int)nkp, v8t, v_scale, vbf, st);
   if (e != hipSuccess) return QATTN_EHIP;
   BshdView qv{q, 0, q_str[0], q_str[1]};
   e = launch_quant_i8(qv, nullptr, 1, H, Nq, D, (int)nqp, q8, q_scale, st);
@@ -233,14 +236,14 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
   a.q_scale = q_scale;
   a.k8 = k_cache;
   a.k_scale = k_tok_scale;
-  a.v8t = v8t;
+  a.vbf = vbf;
   a.v_scale = v_scale;
   a.out = out;
   a.q8_bh = nqp * D;
   a.qs_bh = nqp / kBlk;
   a.k8_bh = (int64_t)Nk * D;
   a.ks_bh = Nk;
-  a.v8t_bh = (int64_t)D * nkp;
+  a.vbf_bh = (int64_t)D * nkp;
   a.ldv = nkp;
   a.out_sb = 0;
   a.out_sn = out_str[0];

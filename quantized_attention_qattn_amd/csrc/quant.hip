@@ -187,7 +187,7 @@ __global__ __launch_bounds__(D) void v_amax_final(int nchunk, int64_t region, co
 
 template <int D, bool CACHE>
 __global__ __launch_bounds__(kThreads) void v_encode(BshdView v, const int8_t* cache, const float* tok_scale, int H,
-                                                     int N, int npad, const float* v_amax, uint8_t* v8t) {
+                                                     int N, int npad, const float* v_amax, uint8_t* v8t, uint16_t* vbf) {
   constexpr int CPR = D / 8, RPP = kThreads / CPR, PASSES = kBlk / RPP;
   constexpr int PITCH = kBlk + 16;  // transpose buffer row pitch (bytes)
   __shared__ __align__(16) uint8_t sT[D * PITCH];
@@ -227,7 +227,19 @@ __global__ __launch_bounds__(kThreads) void v_encode(BshdView v, const int8_t* c
   constexpr int CHUNKS = D * (kBlk / 16);
   for (int id = t; id < CHUNKS; id += kThreads) {
     const int c = id >> 2, part = id & 3;
-    *(v4i*)(v8t + (bh * D + c) * npad + n0 + 16 * part) = *(const v4i*)(sT + c * PITCH + 16 * part);
+    const v4i w = *(const v4i*)(sT + c * PITCH + 16 * part);
+    *(v4i*)(v8t + (bh * D + c) * npad + n0 + 16 * part) = w;
+    if (vbf) {  // the exact bf16 values of the 16 codes (every e4m3 value is a bf16 value)
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        b[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false));
+        b[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true));
+      }
+      uint16_t* dst = vbf + (bh * D + c) * npad + n0 + 16 * part;
+      *(v4i*)dst = v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+      *(v4i*)(dst + 8) = v4i{(int)b[4], (int)b[5], (int)b[6], (int)b[7]};
+    }
   }
 }
 
@@ -330,28 +342,28 @@ hipError_t launch_kv_append_i8(const void* x, int64_t sn, int64_t sh, int Nnew, 
 
 template <int D, bool CACHE>
 static void quant_v_impl(BshdView v, const int8_t* cache, const float* tok_scale, int B, int H, int N, int npad,
-                         uint8_t* v8t, float* v_scale, hipStream_t st) {
+                         uint8_t* v8t, float* v_scale, uint16_t* vbf, hipStream_t st) {
   const int64_t region = (int64_t)npad * D;  // bytes of v8t per (b, h)
   const int nc = nchunks(N);
   v_amax_partial<D, CACHE><<<dim3(nc, H, B), kThreads, 0, st>>>(v, cache, tok_scale, H, N, region, v8t);
   v_amax_final<D><<<B * H, D, 0, st>>>(nc, region, v8t, v_scale);
-  v_encode<D, CACHE><<<dim3(npad / kBlk, H, B), kThreads, 0, st>>>(v, cache, tok_scale, H, N, npad, v_scale, v8t);
+  v_encode<D, CACHE><<<dim3(npad / kBlk, H, B), kThreads, 0, st>>>(v, cache, tok_scale, H, N, npad, v_scale, v8t, vbf);
   const int64_t n = (int64_t)B * H * D;
   v_scale_from_amax<<<(int)((n + 255) / 256), 256, 0, st>>>(v_scale, n);
 }
 
 hipError_t launch_quant_v(BshdView v, const int8_t* cache, const float* tok_scale, int B, int H, int N, int D,
-                          int npad, uint8_t* v8t, float* v_scale, hipStream_t st) {
+                          int npad, uint8_t* v8t, float* v_scale, uint16_t* vbf, hipStream_t st) {
   if (D == 128) {
     if (cache)
-      quant_v_impl<128, true>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, st);
+      quant_v_impl<128, true>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, vbf, st);
     else
-      quant_v_impl<128, false>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, st);
+      quant_v_impl<128, false>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, vbf, st);
   } else {
     if (cache)
-      quant_v_impl<64, true>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, st);
+      quant_v_impl<64, true>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, vbf, st);
     else
-      quant_v_impl<64, false>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, st);
+      quant_v_impl<64, false>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, vbf, st);
   }
   return hipGetLastError();
 }

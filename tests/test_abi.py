@@ -28,7 +28,7 @@ def lib():
     L = ct.CDLL(LIB)
     P, I, F = ct.c_void_p, ct.c_int, ct.c_float
     L.qattn_quant_qk.argtypes = [P, I64x3, P, I64x3, I, I, I, I, I, P, P, P, P, P, P]
-    L.qattn_quant_v.argtypes = [P, I64x3, I, I, I, I, P, P, P]
+    L.qattn_quant_v.argtypes = [P, I64x3, I, I, I, I, P, P, P, P]
     L.qattn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P, I64x3, I, P]
     L.qattn_fwd_i8kv.argtypes = [P, I64x2, P, P, P, P, I, I, I, I, I, F, I, P, ct.c_size_t, P, I64x2, I, P]
     L.qattn_fwd_i8kv_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -67,13 +67,13 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # H*D*Nk_pad + H*D*4 + H*Nq_pad*D + H*Nq_pad/64*4, each rounded up to 256 bytes
+    # H*D*Nk_pad + H*D*4 + H*Nq_pad*D + H*Nq_pad/64*4 + H*D*Nk_pad*2, each rounded up to 256 bytes
     H, Nq, Nk, D = 32, 1024, 32768, 128
-    expect = H * D * Nk + H * D * 4 + H * Nq * D + ((H * Nq // 64 * 4 + 255) // 256) * 256
+    expect = H * D * Nk + H * D * 4 + H * Nq * D + ((H * Nq // 64 * 4 + 255) // 256) * 256 + H * D * Nk * 2
     assert lib.qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, 1) == expect
     # split-KV adds S*H*Nq_pad*D*4 (partial O) + S*H*Nq_pad*8 (m, d')
     assert lib.qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, 4) == expect + 4 * H * Nq * D * 4 + 4 * H * Nq * 8
-    assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 64, 1) == 2 * 64 * 64 + 512 + 2 * 64 * 64 + 256
+    assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 64, 1) == 2 * 64 * 64 + 512 + 2 * 64 * 64 + 256 + 2 * 64 * 64 * 2
     assert lib.qattn_fwd_i8kv_workspace_bytes(0, 1, 1, 64, 1) == 0
     assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 96, 1) == 0
     assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 64, 0) == 0
@@ -115,9 +115,10 @@ def test_quant_qk_validation(lib):
 
 def test_quant_v_validation(lib):
     st = I64x3(1024, 128, 64)
-    assert lib.qattn_quant_v(None, st, 1, 2, 64, 64, A, A, None) == EINVAL
-    assert lib.qattn_quant_v(A, st, 1, 2, 64, 80, A, A, None) == EUNSUP
-    assert lib.qattn_quant_v(A, st, 1, 2, 64, 64, A + 1, A, None) == EINVAL
+    assert lib.qattn_quant_v(None, st, 1, 2, 64, 64, A, A, None, None) == EINVAL
+    assert lib.qattn_quant_v(A, st, 1, 2, 64, 80, A, A, None, None) == EUNSUP
+    assert lib.qattn_quant_v(A, st, 1, 2, 64, 64, A + 1, A, None, None) == EINVAL
+    assert lib.qattn_quant_v(A, st, 1, 2, 64, 64, A, A, A + 16, None) == EINVAL  # vbf not 256-byte aligned
 
 
 def test_fwd_validation(lib):

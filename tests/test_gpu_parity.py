@@ -108,6 +108,7 @@ def test_quant_v_bit_exact(qa, B, H, Nq, Nk, D):
     v8t, vs = oracle.quant_v(v)
     assert np.array_equal(host(t["v8t"]), v8t)
     assert np.array_equal(host(t["v_scale"]).view(np.uint32), vs.view(np.uint32))
+    assert np.array_equal(host(t["vbf"]), host(vbf_of(v8t)))  # the codes' exact bf16 values
 
 
 def test_quant_v_every_bf16_value(qa):
@@ -156,11 +157,18 @@ def test_p8_codes_whole_grid(qa):
 # ----------------------------------------------------------------------------------
 # fused loop
 # ----------------------------------------------------------------------------------
+def vbf_of(v8t: np.ndarray) -> torch.Tensor:
+    """The bf16 values of e4m3 codes (exact), as qattn_quant_v's vbf output holds them."""
+    dec = oracle.e4m3_decode_table().astype(np.float32)
+    return dev_bf16(W.bf16_bits(dec[v8t]))
+
+
 def run_fwd(qa, ops, Nq, Nk, lam, causal, out_dtype=torch.float32):
-    q8, qs, k8, ks, v8t, vs = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in ops]
+    q8, qs, k8, ks, vs = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (ops[0], ops[1], ops[2], ops[3], ops[5])]
+    vbf = vbf_of(np.ascontiguousarray(ops[4]))
     B, H, _, D = q8.shape
     out = torch.empty((B, Nq, H, D), dtype=out_dtype, device="cuda")
-    qa.qattn_fwd(q8, qs, k8, ks, v8t, vs, Nq, Nk, out, lam, causal)
+    qa.qattn_fwd(q8, qs, k8, ks, vbf, vs, Nq, Nk, out, lam, causal)
     torch.cuda.synchronize()
     return host(out)
 
@@ -416,13 +424,13 @@ def test_fwd_head_split_bit_identical(qa, causal):
     t = qa.alloc_qk(1, H, Nq, Nk, D)
     tv = qa.alloc_v(1, H, Nk, D)
     qa.qattn_quant_qk(q, k, t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["k_mean"])
-    qa.qattn_quant_v(v, tv["v8t"], tv["v_scale"])
+    qa.qattn_quant_v(v, tv["v8t"], tv["v_scale"], tv["vbf"])
     whole = torch.empty((1, Nq, H, D), dtype=torch.float32, device="cuda")
     parts = torch.empty_like(whole)
-    qa.qattn_fwd(t["q8"], t["q_scale"], t["k8"], t["k_scale"], tv["v8t"], tv["v_scale"], Nq, Nk, whole, 0.0, causal)
+    qa.qattn_fwd(t["q8"], t["q_scale"], t["k8"], t["k_scale"], tv["vbf"], tv["v_scale"], Nq, Nk, whole, 0.0, causal)
     for h in range(0, H, step):
         sl = slice(h, h + step)
-        qa.qattn_fwd(t["q8"][:, sl], t["q_scale"][:, sl], t["k8"][:, sl], t["k_scale"][:, sl], tv["v8t"][:, sl],
+        qa.qattn_fwd(t["q8"][:, sl], t["q_scale"][:, sl], t["k8"][:, sl], t["k_scale"][:, sl], tv["vbf"][:, sl],
                      tv["v_scale"][:, sl], Nq, Nk, parts[:, :, sl], 0.0, causal)
     torch.cuda.synchronize()
     assert torch.equal(whole.view(torch.int32), parts.view(torch.int32))
@@ -436,7 +444,7 @@ def test_binding_rejects_strided_code_buffers(qa):
     out = torch.empty((2, 64, 2, 64), dtype=torch.float32, device="cuda")
     sl = slice(0, 2)
     with pytest.raises(ValueError):
-        qa.qattn_fwd(t["q8"][:, sl], t["q_scale"][:, sl], t["k8"][:, sl], t["k_scale"][:, sl], tv["v8t"][:, sl],
+        qa.qattn_fwd(t["q8"][:, sl], t["q_scale"][:, sl], t["k8"][:, sl], t["k_scale"][:, sl], tv["vbf"][:, sl],
                      tv["v_scale"][:, sl], 64, 64, out)
 
 
