@@ -40,6 +40,7 @@
 //   j at ticks 2j (group 0) and 2j + 1 (group 1); the buffer is reloaded at tick 2j + 3.
 #include <climits>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -76,35 +77,64 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_bit_cast(int, w);
 }
 
+// Puts a wave-uniform value in an SGPR as an opaque operand.  A buffer load's soffset
+// (and M0) must be an SGPR or a small inline constant: a value the compiler has folded
+// to a larger constant would otherwise reach the assembly below as a literal, and one
+// it cannot prove uniform would sit in a VGPR.
+__device__ __forceinline__ void sgpr_value(uint32_t& x) {
+  x = __builtin_amdgcn_readfirstlane(x);
+  asm volatile("" : "+s"(x));
+}
+__device__ __forceinline__ void sgpr_value(int& x) {
+  x = __builtin_amdgcn_readfirstlane(x);
+  asm volatile("" : "+s"(x));
+}
+
 // Direct global -> LDS load of 16 bytes per lane: lane l of the wave writes LDS bytes
-// [lds + 16 l, lds + 16 l + 16).  Issued as inline assembly so that the compiler does
-// not order the kernel's LDS reads after it (it would have to assume that the
-// asynchronous LDS write may alias them); completion is awaited explicitly with
-// s_waitcnt vmcnt(0) and a barrier before the buffer is read.  M0 (the LDS base) is
-// saved and restored around the load.
+// [lds + OFF + 16 l, lds + OFF + 16 l + 16).  Issued as inline assembly so that the
+// compiler does not order the kernel's LDS reads after it (it would have to assume that
+// the asynchronous LDS write may alias them); completion is awaited explicitly with
+// s_waitcnt vmcnt(0) and a barrier before the buffer is read.  M0 (the LDS address) is
+// formed inside the assembly from one base register and the constant OFF, so that no
+// register holds a precomputed address per buffer and segment, and is restored after.
+template <int OFF>
 __device__ __forceinline__ void dma_16B(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voffset, int soffset) {
   uint32_t saved;
+  sgpr_value(lds);
+  sgpr_value(soffset);
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_add_u32 m0, %1, %5\n\t"
       "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(voffset), "s"(rsrc), "s"(soffset)
-      : "memory");
+      : "s"(lds), "v"(voffset), "s"(rsrc), "s"(soffset), "i"(OFF)
+      : "memory", "scc");
 }
-// The same with 4 bytes per lane: lane l writes LDS bytes [lds + 4 l, lds + 4 l + 4).
+// The same with 4 bytes per lane: lane l writes LDS bytes [lds + OFF + 4 l, ... + 4).
 // Each dword is range-checked on its own (reads past the end of the resource give 0).
+template <int OFF>
 __device__ __forceinline__ void dma_4B(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, int voffset, int soffset) {
   uint32_t saved;
+  sgpr_value(lds);
+  sgpr_value(soffset);
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_add_u32 m0, %1, %5\n\t"
       "buffer_load_dword %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(voffset), "s"(rsrc), "s"(soffset)
-      : "memory");
+      : "s"(lds), "v"(voffset), "s"(rsrc), "s"(soffset), "i"(OFF)
+      : "memory", "scc");
+}
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N - 1.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 // wave-uniform LDS byte address of a shared-memory location
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -169,6 +199,34 @@ __device__ __forceinline__ float sum_with_partner(float x) {
 constexpr float kAccBiasF = 12582912.0f;
 __device__ __forceinline__ float acc_f32(int biased) { return __builtin_bit_cast(float, biased) - kAccBiasF; }
 
+// x if key I of the lane's 32 keys is visible (I <= lim), else `masked` (a VGPR: with
+// VCC the select may read no other scalar operand), or 0 in the second form: compare
+// and select in one piece of assembly.  Written as C++, the compiler computes the 32
+// compares of a masked tile ahead of their uses and keeps each result in a 64-bit
+// scalar mask register; that pressure makes it spill scalar registers throughout the
+// tile loop.  The s_nop gives the two wait states that a VALU write of VCC needs before
+// a VALU read of it.
+template <int I>
+__device__ __forceinline__ int select_visible(int x, int lim, int masked) {
+  asm("v_cmp_le_i32 vcc, %2, %1\n\t"
+      "s_nop 1\n\t"
+      "v_cndmask_b32_e64 %0, %3, %0, vcc"
+      : "+v"(x)
+      : "v"(lim), "i"(I), "v"(masked)
+      : "vcc");
+  return x;
+}
+template <int I>
+__device__ __forceinline__ int select_visible_or_zero(int x, int lim) {
+  asm("v_cmp_le_i32 vcc, %2, %1\n\t"
+      "s_nop 1\n\t"
+      "v_cndmask_b32_e64 %0, 0, %0, vcc"
+      : "+v"(x)
+      : "v"(lim), "i"(I)
+      : "vcc");
+  return x;
+}
+
 // Online-softmax update of one 64-key tile for this lane's query and its 32 keys
 // (key0 + i, i = 16 kb + j held in S_kb[j]).  Returns the 32 FP8 codes of P' = 256 P
 // packed as the B operand of the PV MFMA; updates m, the lane's share of d'' = 2^80 d',
@@ -187,28 +245,42 @@ __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, cons
       cvec[i + 3] = c4.w;
     }
   }
-  auto acc_of = [&](int i) { return i < 16 ? S0[i] : S1[i - 16]; };
-  auto vis = [&](int i) { return !MASKED || key0 + i <= vis_last; };
+  // masked tile: key i of this lane is visible iff i <= lim.  A hidden key's
+  // accumulator reads as 0 (below every biased accumulator) for the tile max and its
+  // exponent argument as -inf, so that its P is exactly 0 whatever the scale.
+  const int lim = vis_last - key0;
+  const int ninf = (int)0xff800000u;
+  int accv[32];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    accv[i] = S0[i];
+    accv[16 + i] = S1[i];
+  }
   float Mt;
   if (PER_TOKEN) {
     Mt = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float sv = acc_f32(acc_of(i)) * cvec[i];
-      Mt = vis(i) ? fmaxf(Mt, sv) : Mt;
-    }
+    static_for<32>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      float sv = acc_f32(accv[i]) * cvec[i];
+      if (MASKED) sv = __builtin_bit_cast(float, select_visible<i>(__builtin_bit_cast(int, sv), lim, ninf));
+      Mt = fmaxf(Mt, sv);
+    });
     Mt = fmax_with_partner(Mt);
   } else {
-    int mx = INT_MIN;
-    if (!MASKED) {
+    int am[32];
+    static_for<32>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      am[i] = MASKED ? select_visible_or_zero<i>(accv[i], lim) : accv[i];
+    });
+    // two chains of three-input maxima (v_max3_i32): 17 instructions for 32 values
+    int mxa = INT_MIN, mxb = INT_MIN;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = max(mx, max(S0[i], S1[i]));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) mx = vis(i) ? max(mx, acc_of(i)) : mx;
+    for (int i = 0; i < 16; i += 2) {
+      mxa = max(max(mxa, am[i]), am[i + 1]);
+      mxb = max(max(mxb, am[16 + i]), am[16 + i + 1]);
     }
-    mx = max_with_partner(mx);
-    Mt = mx == INT_MIN ? -INFINITY : acc_f32(mx) * c_tile;
+    const int mx = max_with_partner(max(mxa, mxb));
+    Mt = mx <= 0 ? -INFINITY : acc_f32(mx) * c_tile;  // <= 0: every key of the row hidden
   }
   const float mnew = fmaxf(m, Mt);
   const float ms = mnew == -INFINITY ? 0.0f : mnew;
@@ -220,19 +292,16 @@ __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, cons
   // i.e. 2^80 times an fp32 sum of P')
   float ds[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   v8i pf;
+  float p[32];
+  static_for<32>([&](auto i_c) {
+    constexpr int i = decltype(i_c)::value;
+    float u = __builtin_fmaf(acc_f32(accv[i]), PER_TOKEN ? cvec[i] : c_tile, bconst);
+    if (MASKED) u = __builtin_bit_cast(float, select_visible<i>(__builtin_bit_cast(int, u), lim, ninf));
+    p[i] = p_from_u(u);
+    ds[i & 3] += p[i];
+  });
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    float p[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * w + e;
-      float pv = p_from_u(__builtin_fmaf(acc_f32(acc_of(i)), PER_TOKEN ? cvec[i] : c_tile, bconst));
-      if (MASKED) pv = vis(i) ? pv : 0.0f;
-      ds[e] += pv;
-      p[e] = pv;
-    }
-    pf[w] = pack_fp8x4(p[0], p[1], p[2], p[3]);
-  }
+  for (int w = 0; w < 8; ++w) pf[w] = pack_fp8x4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3]);
   dsum = dsum * alpha + ((ds[0] + ds[1]) + (ds[2] + ds[3]));
   return pf;
 }
@@ -271,7 +340,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   __shared__ __align__(16) float sC[2][QB][BN];     // PER_TOKEN: c_j per (buffer, query block, key)
   __shared__ __align__(16) float sKs[NBUF][BN];     // PER_TOKEN: raw K scales of each slot
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
   const int grp = wave >> 2;  // group 0 loads the tiles and leads by one phase
   const int gtid = tid & 255;  // thread index within the group
   const int l32 = lane & 31, hh = lane >> 5;
@@ -361,20 +431,22 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   // loads: a compiler-visible load whose value is used while tile loads are in flight
   // would make the compiler wait for all of them.
   // LDS byte addresses of the buffers, formed once (wave-uniform)
-  const uint32_t ldsK0 = lds_addr(&sK[0][0]), ldsV0 = lds_addr(&sVb[0][0]), ldsKs0 = lds_addr(&sKs[0][0]);
-  auto stage = [&](int t, int buf) {
-    if (PER_TOKEN && t < ntiles) dma_4B(srs, ldsKs0 + buf * (4 * BN), 4 * lane, 4 * (t0 + t) * BN);
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      // wave-uniform; readfirstlane tells the compiler so (the asm needs an SGPR)
-      const uint32_t seg = __builtin_amdgcn_readfirstlane(1024u * ((wave & 3) * PT + i));
-      if (t < ntiles) dma_16B(krs, ldsK0 + buf * (BN * D) + seg, koff[i], (t0 + t) * BN * D);
-    }
-#pragma unroll
-    for (int i = 0; i < PTV; ++i) {
-      const uint32_t seg = __builtin_amdgcn_readfirstlane(1024u * ((wave & 3) * PTV + i));
-      if (t > 0) dma_16B(vrs, ldsV0 + buf * (2 * D * BN) + seg, voff[i], (t0 + t - 1) * BN * 2);
-    }
+  // LDS byte addresses of this wave's segments of buffer 0 (wave-uniform); the buffer
+  // and segment offsets are immediates of the loads
+  const uint32_t ldsK = lds_addr(&sK[0][0]) + 1024u * ((wave & 3) * PT);
+  const uint32_t ldsV = lds_addr(&sVb[0][0]) + 1024u * ((wave & 3) * PTV);
+  const uint32_t ldsKs = lds_addr(&sKs[0][0]);
+  auto stage = [&](int t, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    if (PER_TOKEN && t < ntiles) dma_4B<buf * (4 * BN)>(srs, ldsKs, 4 * lane, 4 * (t0 + t) * BN);
+    static_for<PT>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      if (t < ntiles) dma_16B<buf * (BN * D) + 1024 * i>(krs, ldsK, koff[i], (t0 + t) * BN * D);
+    });
+    static_for<PTV>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      if (t > 0) dma_16B<buf * (2 * D * BN) + 1024 * i>(vrs, ldsV, voff[i], (t0 + t - 1) * BN * 2);
+    });
   };
   // wait until at most the loads of slot t are in flight (t > ntiles: none)
   static_assert(PT + PTV + 1 < 64, "vmcnt immediate");
@@ -412,8 +484,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   // loads in flight
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   if (grp == 0 && ntiles > 0) {
-    stage(0, 0);
-    stage(1, 1);
+    stage(0, std::integral_constant<int, 0>{});
+    stage(1, std::integral_constant<int, 1>{});
     wait_all_but(1);
     scale_store(0, 0);
   }
@@ -425,11 +497,13 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   const int nkb = (a.Nk + BN - 1) / BN;  // K scale blocks
   float ks_next = (!PER_TOKEN && ntiles > 0) ? ks_const[t0] : 0.0f;
   if (grp == 1) phase_barrier();
-  int buf = 0;  // buffer of slot i
-  for (int i = 0; i <= ntiles; ++i) {
+  // One iteration of the tile loop for slot i, which sits in buffer BUF = i % NBUF.  The
+  // loop is unrolled NBUF times so that the buffer offsets of every LDS access are
+  // immediates: the per-lane addresses stay in registers and no iteration recomputes them.
+  auto iteration = [&](const int i, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr int buf1 = (buf + 1) % NBUF, buf2 = (buf + 2) % NBUF;
     // ---- MFMA phase i: S = K_i . Q^T and O^T += V_{i-1}^T . P_{i-1}^T ----
-    const int buf1 = buf == NBUF - 1 ? 0 : buf + 1;
-    const int buf2 = buf1 == NBUF - 1 ? 0 : buf1 + 1;
     // The MFMA phase has one branch-free form: the first one runs PV on a zeroed V^T
     // buffer with P = 0, the last one computes a QK that nobody reads, and a wave whose
     // rows see no key of the tile has P = 0 (separate forms would make the compiler copy
@@ -490,7 +564,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     phase_barrier();
 
     // ---- VALU phase i: online softmax of tile i ----
-    if (grp == 0 && i + 2 <= ntiles) stage(i + 2, buf2);
+    if (grp == 0 && i + 2 <= ntiles) stage(i + 2, std::integral_constant<int, buf2>{});
     // per-tile K scale of this tile (loaded during the previous VALU phase) and of the
     // next one: uniform addresses read through the constant address space, i.e. scalar
     // loads, issued a phase ahead so that their latency is never waited for
@@ -531,7 +605,15 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
       if (i + 1 < ntiles) scale_store(i + 1, buf1);
     }
     phase_barrier();
-    buf = buf1;
+  };
+  static_assert(NBUF == 3, "the tile loop is unrolled once per buffer");
+  for (int i = 0;;) {
+    iteration(i, std::integral_constant<int, 0>{});
+    if (++i > ntiles) break;
+    iteration(i, std::integral_constant<int, 1>{});
+    if (++i > ntiles) break;
+    iteration(i, std::integral_constant<int, 2>{});
+    if (++i > ntiles) break;
   }
   if (grp == 0) phase_barrier();
 
