@@ -1,7 +1,7 @@
 """Benchmark of the quantized attention forward on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-  dense workloads:   qattn_quant_qk -> qattn_quant_v -> qattn_fwd
+  dense workloads:   qattn_prep (fused preparation of Q, K, V) -> qattn_fwd
   prefill workloads: qattn_fwd_i8kv (q quantization, cache V requantization, fused loop)
 The printed JSON line reports whole-step throughput as attention TOPS
 (4 * N_q * N_k * D * H per step, visible pairs only for causal workloads), the fused
@@ -156,8 +156,8 @@ def main():
         ev_pairs = []
 
         def step(record):
-            qa.qattn_quant_qk(dq, dk, t_qk["q8"], t_qk["q_scale"], t_qk["k8"], t_qk["k_scale"], t_qk["k_mean"])
-            qa.qattn_quant_v(dv, t_v["v8t"], t_v["v_scale"], t_v["vbf"])
+            qa.qattn_prep(dq, dk, dv, t_qk["q8"], t_qk["q_scale"], t_qk["k8"], t_qk["k_scale"], t_qk["k_mean"],
+                          t_v["v8t"], t_v["v_scale"], t_v["vbf"])
             if record:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
@@ -222,7 +222,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.Nq, "N_k": w.Nk, "D": w.D,
                    "causal": w.causal, "pos0": w.pos0 if w.kind == "i8kv" else None,
                    "kv_splits": kv_splits if w.kind == "i8kv" else 1,
-                   "step": "quant_qk + quant_v + fwd" if w.kind == "dense" else "fwd_i8kv (incl. q quant, V requant)",
+                   "step": "prep + fwd" if w.kind == "dense" else "fwd_i8kv (incl. q quant, V requant)",
                    "input_sha256": in_sha},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel" if w.kind == "dense" else "fwd_i8kv call",
                      "achieved": round(achieved, 3), "peak": PEAK_INT8_FP8_TOPS, "unit": "TFLOP/s",

@@ -76,6 +76,18 @@ int qattn_quant_qk(const void* q, const int64_t q_str[3], const void* k, const i
 int qattn_quant_v(const void* v, const int64_t v_str[3], int B, int H, int Nk, int D, uint8_t* v8t,
                   float* v_scale, uint16_t* vbf, void* stream);
 
+/* Steps 1-2 in one call ("H3 Performance Roadmap", "Phase 4" item 2: a single
+ * preparation pass over the strided inputs in place of separate quantizer and layout
+ * kernels): the outputs of qattn_quant_qk followed by qattn_quant_v, byte for byte, from
+ * four launches instead of eight.  Q is read once; K and V twice (the channel mean and
+ * the channel absmax need every token before any token is coded).  Arguments, layouts
+ * and alignment are those of the two calls; vbf may be NULL.  k8 and v8t hold partial
+ * results during the call.  Returns QATTN_EINVAL / QATTN_EUNSUPPORTED before any launch
+ * on a bad argument. */
+int qattn_prep(const void* q, const int64_t q_str[3], const void* k, const int64_t k_str[3], const void* v,
+               const int64_t v_str[3], int B, int H, int Nq, int Nk, int D, int8_t* q8, float* q_scale, int8_t* k8,
+               float* k_scale, float* k_mean, uint8_t* v8t, float* v_scale, uint16_t* vbf, void* stream);
+
 /* Steps 3-5 -- fused INT8 QK, online softmax with FP8 P, PV and epilogue ("Sage2 SM89
  * Temporal Pair Experiment", "Candidate": per 64-key tile QK -> update m, d, O ->
  * accumulate d -> P to 8 bit -> PV), on the outputs of steps 1-2 (same layouts).

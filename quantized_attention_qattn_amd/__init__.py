@@ -40,6 +40,9 @@ _lib.qattn_quant_qk.argtypes = [_P, _I64x3, _P, _I64x3, _I, _I, _I, _I, _I, _P, 
 _lib.qattn_quant_qk.restype = _I
 _lib.qattn_quant_v.argtypes = [_P, _I64x3, _I, _I, _I, _I, _P, _P, _P, _P]
 _lib.qattn_quant_v.restype = _I
+_lib.qattn_prep.argtypes = [_P, _I64x3, _P, _I64x3, _P, _I64x3, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                            _P]
+_lib.qattn_prep.restype = _I
 _lib.qattn_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I64x3, _I, _P]
 _lib.qattn_fwd.restype = _I
 _lib.qattn_fwd_i8kv.argtypes = [_P, _I64x2, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P, _I64x2, _I, _P]
@@ -130,6 +133,29 @@ def qattn_quant_v(v, v8t, v_scale, vbf=None, stream=None) -> None:
         _buf(vbf, torch.bfloat16, (B, H, D, npad(Nk)), "vbf")
     _check(_lib.qattn_quant_v(_ptr(v), _I64x3(*v.stride()[:3]), B, H, Nk, D, _ptr(v8t), _ptr(v_scale),
                               None if vbf is None else _ptr(vbf), _stream(stream)), "qattn_quant_v")
+
+
+def qattn_prep(q, k, v, q8, q_scale, k8, k_scale, k_mean, v8t, v_scale, vbf=None, stream=None) -> None:
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    _need(v, torch.bfloat16, "v")
+    B, Nq, H, D = q.shape
+    Nk = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != H or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q, k and v must agree on B, H, D (and k, v on N)")
+    _buf(q8, torch.int8, (B, H, npad(Nq), D), "q8")
+    _buf(q_scale, torch.float32, (B, H, npad(Nq) // BLOCK), "q_scale")
+    _buf(k8, torch.int8, (B, H, npad(Nk), D), "k8")
+    _buf(k_scale, torch.float32, (B, H, npad(Nk) // BLOCK), "k_scale")
+    _buf(k_mean, torch.float32, (B, H, D), "k_mean")
+    _buf(v8t, torch.uint8, (B, H, D, npad(Nk)), "v8t")
+    _buf(v_scale, torch.float32, (B, H, D), "v_scale")
+    if vbf is not None:
+        _buf(vbf, torch.bfloat16, (B, H, D, npad(Nk)), "vbf")
+    _check(_lib.qattn_prep(_ptr(q), _I64x3(*q.stride()[:3]), _ptr(k), _I64x3(*k.stride()[:3]), _ptr(v),
+                           _I64x3(*v.stride()[:3]), B, H, Nq, Nk, D, _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
+                           _ptr(k_mean), _ptr(v8t), _ptr(v_scale), None if vbf is None else _ptr(vbf),
+                           _stream(stream)), "qattn_prep")
 
 
 def qattn_fwd(q8, q_scale, k8, k_scale, vbf, v_scale, Nq: int, Nk: int, out, scale_log2: float = 0.0,
@@ -232,15 +258,24 @@ def quant_v(v, stream=None):
     return t
 
 
-def attention(q, k, v, causal: bool = False, scale_log2: float = 0.0, out_dtype=torch.bfloat16, stream=None):
-    """Steps 1-5 on bf16 [B, N, H, D] views; returns (out [B, Nq, H, D], intermediates)."""
+def prep(q, k, v, stream=None):
+    """Steps 1-2 through the fused preparation; returns the intermediates of quant_qk and quant_v."""
     B, Nq, H, D = q.shape
-    qk = quant_qk(q, k, stream)
-    vv = quant_v(v, stream)
+    t = {**alloc_qk(B, H, Nq, k.shape[1], D, q.device), **alloc_v(B, H, k.shape[1], D, q.device)}
+    qattn_prep(q, k, v, t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["k_mean"], t["v8t"], t["v_scale"], t["vbf"],
+               stream)
+    return t
+
+
+def attention(q, k, v, causal: bool = False, scale_log2: float = 0.0, out_dtype=torch.bfloat16, stream=None):
+    """Steps 1-5 on bf16 [B, N, H, D] views (fused preparation, then the fused loop);
+    returns (out [B, Nq, H, D], intermediates)."""
+    B, Nq, H, D = q.shape
+    qk = prep(q, k, v, stream)
     out = torch.empty((B, Nq, H, D), dtype=out_dtype, device=q.device)
-    qattn_fwd(qk["q8"], qk["q_scale"], qk["k8"], qk["k_scale"], vv["vbf"], vv["v_scale"], Nq, k.shape[1], out,
+    qattn_fwd(qk["q8"], qk["q_scale"], qk["k8"], qk["k_scale"], qk["vbf"], qk["v_scale"], Nq, k.shape[1], out,
               scale_log2, causal, stream)
-    return out, {**qk, **vv}
+    return out, qk
 
 
 def attention_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, scale_log2: float = 0.0,
@@ -255,5 +290,5 @@ def attention_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, sca
     return out, ws
 
 
-__all__ = [n for n in dir() if n.startswith("qattn_")] + ["attention", "attention_i8kv", "quant_qk", "quant_v",
+__all__ = [n for n in dir() if n.startswith("qattn_")] + ["attention", "attention_i8kv", "prep", "quant_qk", "quant_v",
                                                            "alloc_qk", "alloc_v", "QattnError", "LIB_PATH"]

@@ -72,6 +72,25 @@ hipError_t launch_quant_i8(BshdView x, const float* mean, int B, int H, int N, i
 hipError_t launch_quant_v(BshdView v, const int8_t* cache, const float* tok_scale, int B, int H, int N, int D,
                           int npad, uint8_t* v8t, float* v_scale, uint16_t* vbf, hipStream_t st);
 
+// Fused preparation (pass 1, final, pass 2, scale).  Dense form: q, k, v bf16 views with
+// k8 != nullptr; prefill form: q view (b = 0) and the int8 V cache with per-token scales,
+// k8 == nullptr.  Partial results live in the k8 and v8t regions until pass 2 writes them.
+struct PrepArgs {
+  BshdView q, k, v;
+  int B, H, Nq, Nk;
+  int8_t* q8;
+  float* q_scale;
+  int8_t* k8;
+  float* k_scale;
+  float* k_mean;
+  const int8_t* v_cache;
+  const float* v_tok_scale;
+  uint8_t* v8t;
+  float* v_scale;
+  uint16_t* vbf;
+};
+hipError_t launch_prep(const PrepArgs& p, int D, hipStream_t st);
+
 struct FwdArgs {
   const int8_t* q8;
   const float* q_scale;

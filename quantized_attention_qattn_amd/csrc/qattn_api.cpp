@@ -98,6 +98,34 @@ int qattn_quant_v(const void* v, const int64_t v_str[3], int B, int H, int Nk, i
                                   (hipStream_t)stream));
 }
 
+int qattn_prep(const void* q, const int64_t q_str[3], const void* k, const int64_t k_str[3], const void* v,
+               const int64_t v_str[3], int B, int H, int Nq, int Nk, int D, int8_t* q8, float* q_scale, int8_t* k8,
+               float* k_scale, float* k_mean, uint8_t* v8t, float* v_scale, uint16_t* vbf, void* stream) {
+  if (!q8 || !q_scale || !k8 || !k_scale || !k_mean || !v8t || !v_scale) return QATTN_EINVAL;
+  if (!bf16_view_ok(q, q_str, 3) || !bf16_view_ok(k, k_str, 3) || !bf16_view_ok(v, v_str, 3)) return QATTN_EINVAL;
+  if (!sizes_ok(B, H, Nq) || !sizes_ok(B, H, Nk)) return QATTN_EINVAL;
+  if (D != 64 && D != 128) return QATTN_EUNSUPPORTED;
+  if (!aligned(q8, 256) || !aligned(k8, 256) || !aligned(v8t, 256) || (vbf && !aligned(vbf, 256))) return QATTN_EINVAL;
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4) || !aligned(v_scale, 4)) return QATTN_EINVAL;
+  PrepArgs p{};
+  p.q = BshdView{q, q_str[0], q_str[1], q_str[2]};
+  p.k = BshdView{k, k_str[0], k_str[1], k_str[2]};
+  p.v = BshdView{v, v_str[0], v_str[1], v_str[2]};
+  p.B = B;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.q8 = q8;
+  p.q_scale = q_scale;
+  p.k8 = k8;
+  p.k_scale = k_scale;
+  p.k_mean = k_mean;
+  p.v8t = v8t;
+  p.v_scale = v_scale;
+  p.vbf = vbf;
+  return status_of(launch_prep(p, D, (hipStream_t)stream));
+}
+
 static bool out_ok(const void* out, const int64_t* str, int n, int out_dtype) {
   if (!out || !str) return false;
   if (out_dtype != QATTN_OUT_BF16 && out_dtype != QATTN_OUT_F32) return false;
@@ -223,12 +251,22 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
     part_md = (float*)ws;
   }
 
-  // V cache -> per-channel e4m3 (channel-major), q -> INT8 blocks (no smoothing)
-  BshdView none{nullptr, 0, 0, 0};
-  hipError_t e = launch_quant_v(none, v_cache, v_tok_scale, 1, H, Nk, D, (int)nkp, v8t, v_scale, vbf, st);
-  if (e != hipSuccess) return QATTN_EHIP;
-  BshdView qv{q, 0, q_str[0], q_str[1]};
-  e = launch_quant_i8(qv, nullptr, 1, H, Nq, D, (int)nqp, q8, q_scale, st);
+  // q -> INT8 blocks (no smoothing), V cache -> per-channel e4m3 (channel-major) and its
+  // bf16 values: the fused preparation with no K
+  PrepArgs p{};
+  p.q = BshdView{q, 0, q_str[0], q_str[1]};
+  p.B = 1;
+  p.H = H;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.q8 = q8;
+  p.q_scale = q_scale;
+  p.v_cache = v_cache;
+  p.v_tok_scale = v_tok_scale;
+  p.v8t = v8t;
+  p.v_scale = v_scale;
+  p.vbf = vbf;
+  hipError_t e = launch_prep(p, D, st);
   if (e != hipSuccess) return QATTN_EHIP;
 
   FwdArgs a{};

@@ -23,12 +23,16 @@ __device__ __forceinline__ float wave_max(float v) {
 // lives in the k8 region of the same (b, h); pass 2 adds the chunks and divides once.
 // ---------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_mean_partial(BshdView k, int H, int N, int64_t region, int8_t* scratch) {
+struct KSumLds {
+  double red[kThreads / (D / 8)][D];
+};
+template <int D>
+__device__ __forceinline__ void k_mean_partial_body(BshdView k, int H, int N, int64_t region, int8_t* scratch, int chunk,
+                                                    int h, int b, KSumLds<D>& lds) {
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int RPP = kThreads / CPR;  // rows per pass
-  __shared__ double red[RPP][D];
+  auto& red = lds.red;
   const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n0 = chunk * kChunk, n1 = min(N, n0 + kChunk);
   const uint16_t* base = (const uint16_t*)k.p + b * k.sb + h * k.sh + cg * 8;
   double acc[8];
@@ -51,27 +55,39 @@ __global__ __launch_bounds__(kThreads) void k_mean_partial(BshdView k, int H, in
     part[chunk * D + t] = s;
   }
 }
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_mean_partial(BshdView k, int H, int N, int64_t region, int8_t* scratch) {
+  __shared__ KSumLds<D> lds;
+  k_mean_partial_body<D>(k, H, N, region, scratch, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+}
 
+// channel c of one (b, h): the chunk sums added in chunk order (the loop is unrolled so
+// that the loads are issued ahead of the dependent additions)
+template <int D>
+__device__ __forceinline__ float k_mean_of_chunks(const double* part, int nchunk, int N, int c) {
+  double s = 0.0;
+#pragma unroll 8
+  for (int i = 0; i < nchunk; ++i) s += part[i * D + c];
+  return (float)(s / (double)N);
+}
 template <int D>
 __global__ __launch_bounds__(D) void k_mean_final(int N, int nchunk, int64_t region, const int8_t* scratch, float* mean) {
   const int bh = blockIdx.x, c = threadIdx.x;
-  const double* part = (const double*)(scratch + (int64_t)bh * region);
-  double s = 0.0;
-  for (int i = 0; i < nchunk; ++i) s += part[i * D + c];
-  mean[(int64_t)bh * D + c] = (float)(s / (double)N);
+  mean[(int64_t)bh * D + c] = k_mean_of_chunks<D>((const double*)(scratch + (int64_t)bh * region), nchunk, N, c);
 }
 
 // ---------------------------------------------------------------------------------
 // a2: INT8 blocks of 64 rows: a = max|x|, s = a/127, code = rne(x * min(127/a, FLT_MAX)).
 // One workgroup per (block, h, b); each thread keeps its 8-channel slices in registers.
 // ---------------------------------------------------------------------------------
+// wmax: kThreads / 64 floats of LDS, not reused by the workgroup until a barrier has
+// followed this call
 template <int D, bool SMOOTH>
-__global__ __launch_bounds__(kThreads) void quant_i8_blocks(BshdView x, const float* mean, int H, int N, int npad,
-                                                            int8_t* codes, float* scales) {
+__device__ __forceinline__ void quant_i8_block_body(BshdView x, const float* mean, int H, int N, int npad,
+                                                    int8_t* codes, float* scales, int blk, int h, int b,
+                                                    float* wmax) {
   constexpr int CPR = D / 8, RPP = kThreads / CPR, PASSES = kBlk / RPP;
-  __shared__ float wmax[kThreads / 64];
   const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
-  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int r0 = blk * kBlk;
   const int64_t bh = (int64_t)b * H + h;
   const uint16_t* base = (const uint16_t*)x.p + b * x.sb + h * x.sh + cg * 8;
@@ -122,6 +138,12 @@ __global__ __launch_bounds__(kThreads) void quant_i8_blocks(BshdView x, const fl
     *(uint2*)(out + (int64_t)(rl + p * RPP) * D) = make_uint2(wd[0], wd[1]);
   }
 }
+template <int D, bool SMOOTH>
+__global__ __launch_bounds__(kThreads) void quant_i8_blocks(BshdView x, const float* mean, int H, int N, int npad,
+                                                            int8_t* codes, float* scales) {
+  __shared__ float wmax[kThreads / 64];
+  quant_i8_block_body<D, SMOOTH>(x, mean, H, N, npad, codes, scales, blockIdx.x, blockIdx.y, blockIdx.z, wmax);
+}
 
 // ---------------------------------------------------------------------------------
 // a3: per-channel e4m3 V.  Pass 1: per-chunk channel absmax into scratch inside v8t;
@@ -148,13 +170,17 @@ __device__ __forceinline__ void load_v8(BshdView v, const int8_t* cache, const f
   }
 }
 
+template <int D>
+struct VMaxLds {
+  float red[kThreads / (D / 8)][D];
+};
 template <int D, bool CACHE>
-__global__ __launch_bounds__(kThreads) void v_amax_partial(BshdView v, const int8_t* cache, const float* tok_scale,
-                                                           int H, int N, int64_t region, uint8_t* scratch) {
+__device__ __forceinline__ void v_amax_partial_body(BshdView v, const int8_t* cache, const float* tok_scale, int H,
+                                                    int N, int64_t region, uint8_t* scratch, int chunk, int h, int b,
+                                                    VMaxLds<D>& lds) {
   constexpr int CPR = D / 8, RPP = kThreads / CPR;
-  __shared__ float red[RPP][D];
+  auto& red = lds.red;
   const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n0 = chunk * kChunk, n1 = min(N, n0 + kChunk);
   float mx[8];
 #pragma unroll
@@ -175,24 +201,40 @@ __global__ __launch_bounds__(kThreads) void v_amax_partial(BshdView v, const int
     part[chunk * D + t] = m;
   }
 }
+template <int D, bool CACHE>
+__global__ __launch_bounds__(kThreads) void v_amax_partial(BshdView v, const int8_t* cache, const float* tok_scale,
+                                                           int H, int N, int64_t region, uint8_t* scratch) {
+  __shared__ VMaxLds<D> lds;
+  v_amax_partial_body<D, CACHE>(v, cache, tok_scale, H, N, region, scratch, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+}
 
+template <int D>
+__device__ __forceinline__ float v_amax_of_chunks(const float* part, int nchunk, int c) {
+  float m = 0.0f;
+#pragma unroll 8
+  for (int i = 0; i < nchunk; ++i) m = fmaxf(m, part[i * D + c]);
+  return m;
+}
 template <int D>
 __global__ __launch_bounds__(D) void v_amax_final(int nchunk, int64_t region, const uint8_t* scratch, float* v_scale) {
   const int bh = blockIdx.x, c = threadIdx.x;
-  const float* part = (const float*)(scratch + (int64_t)bh * region);
-  float m = 0.0f;
-  for (int i = 0; i < nchunk; ++i) m = fmaxf(m, part[i * D + c]);
-  v_scale[(int64_t)bh * D + c] = m;  // the absmax; converted to the scale after encoding
+  // the absmax; converted to the scale after encoding
+  v_scale[(int64_t)bh * D + c] = v_amax_of_chunks<D>((const float*)(scratch + (int64_t)bh * region), nchunk, c);
 }
 
+constexpr int kEncPitch = kBlk + 16;  // V transpose buffer row pitch (bytes)
+template <int D>
+struct VEncLds {
+  __align__(16) uint8_t sT[D * kEncPitch];
+};
 template <int D, bool CACHE>
-__global__ __launch_bounds__(kThreads) void v_encode(BshdView v, const int8_t* cache, const float* tok_scale, int H,
-                                                     int N, int npad, const float* v_amax, uint8_t* v8t, uint16_t* vbf) {
+__device__ __forceinline__ void v_encode_body(BshdView v, const int8_t* cache, const float* tok_scale, int H, int N,
+                                              int npad, const float* v_amax, uint8_t* v8t, uint16_t* vbf, int tile,
+                                              int h, int b, VEncLds<D>& lds) {
   constexpr int CPR = D / 8, RPP = kThreads / CPR, PASSES = kBlk / RPP;
-  constexpr int PITCH = kBlk + 16;  // transpose buffer row pitch (bytes)
-  __shared__ __align__(16) uint8_t sT[D * PITCH];
+  constexpr int PITCH = kEncPitch;
+  uint8_t* sT = lds.sT;
   const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * H + h;
   const int n0 = tile * kBlk;
   float rc[8];
@@ -242,13 +284,90 @@ __global__ __launch_bounds__(kThreads) void v_encode(BshdView v, const int8_t* c
     }
   }
 }
+template <int D, bool CACHE>
+__global__ __launch_bounds__(kThreads) void v_encode(BshdView v, const int8_t* cache, const float* tok_scale, int H,
+                                                     int N, int npad, const float* v_amax, uint8_t* v8t, uint16_t* vbf) {
+  __shared__ VEncLds<D> lds;
+  v_encode_body<D, CACHE>(v, cache, tok_scale, H, N, npad, v_amax, v8t, vbf, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+}
 
 __global__ void v_scale_from_amax(float* v_scale, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) v_scale[i] = v_scale[i] / 448.0f;
 }
 
-inline int nchunks(int N) { return (N + kChunk - 1) / kChunk; }
+__host__ __device__ inline int nchunks(int N) { return (N + kChunk - 1) / kChunk; }
+
+// ---------------------------------------------------------------------------------
+// Fused preparation ("Phase 4" item 2: one preparation pass over the strided inputs
+// instead of separate quantizer and layout kernels): the steps above in four launches.
+//   pass 1 - per 256-token chunk of one (b, h): the INT8 blocks of Q (the chunk's four
+//            64-row blocks), the fp64 partial sums of K and the partial absmax of V;
+//   final  - per (b, h): the K channel mean and the V channel absmax (parked in v_scale);
+//   pass 2 - per 64-token tile: the INT8 blocks of K - mean, and the e4m3 V tile written
+//            channel-major with its bf16 values;
+//   scale  - v_scale = absmax / 448.
+// Q is read once, K and V twice: a channel's statistics need all of its tokens before
+// any of them is coded.  Every value is computed by the same device code as the
+// separate kernels, in the same order, so the two paths give identical bytes.
+// ---------------------------------------------------------------------------------
+template <int D, bool HAS_K, bool CACHE>
+__global__ __launch_bounds__(kThreads) void prep_pass1(BshdView q, int Nq, int nqpad, int8_t* q8, float* q_scale,
+                                                       BshdView k, BshdView v, const int8_t* v_cache,
+                                                       const float* v_tok_scale, int H, int Nk, int64_t region,
+                                                       int8_t* k_part, uint8_t* v_part) {
+  constexpr int QB = kChunk / kBlk;  // Q blocks per chunk
+  __shared__ float wmax[QB][kThreads / 64];
+  __shared__ KSumLds<D> klds;
+  __shared__ VMaxLds<D> vlds;
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (q8) {
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const int blk = chunk * QB + j;  // uniform over the workgroup: the barrier inside is safe
+      if (blk < nqpad / kBlk) quant_i8_block_body<D, false>(q, nullptr, H, Nq, nqpad, q8, q_scale, blk, h, b, wmax[j]);
+    }
+  }
+  if (chunk < nchunks(Nk)) {
+    if (HAS_K) k_mean_partial_body<D>(k, H, Nk, region, k_part, chunk, h, b, klds);
+    v_amax_partial_body<D, CACHE>(v, v_cache, v_tok_scale, H, Nk, region, v_part, chunk, h, b, vlds);
+  }
+}
+
+template <int D, bool HAS_K>
+__global__ __launch_bounds__(D) void prep_final(int Nk, int nchunk, int64_t region, const int8_t* k_part,
+                                                float* k_mean, const uint8_t* v_part, float* v_amax) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  if (HAS_K) k_mean[(int64_t)bh * D + c] = k_mean_of_chunks<D>((const double*)(k_part + bh * region), nchunk, Nk, c);
+  v_amax[(int64_t)bh * D + c] = v_amax_of_chunks<D>((const float*)(v_part + bh * region), nchunk, c);
+}
+
+template <int D, bool HAS_K, bool CACHE>
+__global__ __launch_bounds__(kThreads) void prep_pass2(BshdView k, const float* k_mean, int8_t* k8, float* k_scale,
+                                                       BshdView v, const int8_t* v_cache, const float* v_tok_scale,
+                                                       const float* v_amax, uint8_t* v8t, uint16_t* vbf, int H,
+                                                       int Nk, int nkpad) {
+  __shared__ float wmax[kThreads / 64];
+  __shared__ VEncLds<D> elds;
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (HAS_K) quant_i8_block_body<D, true>(k, k_mean, H, Nk, nkpad, k8, k_scale, tile, h, b, wmax);
+  v_encode_body<D, CACHE>(v, v_cache, v_tok_scale, H, Nk, nkpad, v_amax, v8t, vbf, tile, h, b, elds);
+}
+
+template <int D, bool HAS_K, bool CACHE>
+static void prep_impl(const PrepArgs& p, hipStream_t st) {
+  const int nqp = p.q8 ? (p.Nq + kBlk - 1) / kBlk * kBlk : 0;
+  const int nkp = (p.Nk + kBlk - 1) / kBlk * kBlk;
+  const int64_t region = (int64_t)nkp * D;  // bytes of k8 and of v8t per (b, h): partial-result scratch
+  const int nck = nchunks(p.Nk), ncq = p.q8 ? nchunks(p.Nq) : 0;
+  prep_pass1<D, HAS_K, CACHE><<<dim3(max(nck, ncq), p.H, p.B), kThreads, 0, st>>>(
+      p.q, p.Nq, nqp, p.q8, p.q_scale, p.k, p.v, p.v_cache, p.v_tok_scale, p.H, p.Nk, region, p.k8, p.v8t);
+  prep_final<D, HAS_K><<<p.B * p.H, D, 0, st>>>(p.Nk, nck, region, p.k8, p.k_mean, p.v8t, p.v_scale);
+  prep_pass2<D, HAS_K, CACHE><<<dim3(nkp / kBlk, p.H, p.B), kThreads, 0, st>>>(
+      p.k, p.k_mean, p.k8, p.k_scale, p.v, p.v_cache, p.v_tok_scale, p.v_scale, p.v8t, p.vbf, p.H, p.Nk, nkp);
+  const int64_t n = (int64_t)p.B * p.H * D;
+  v_scale_from_amax<<<(int)((n + 255) / 256), 256, 0, st>>>(p.v_scale, n);
+}
 
 }  // namespace detail
 using namespace detail;
@@ -364,6 +483,23 @@ hipError_t launch_quant_v(BshdView v, const int8_t* cache, const float* tok_scal
       quant_v_impl<64, true>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, vbf, st);
     else
       quant_v_impl<64, false>(v, cache, tok_scale, B, H, N, npad, v8t, v_scale, vbf, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const PrepArgs& p, int D, hipStream_t st) {
+  const bool has_k = p.k8 != nullptr, cache = p.v_cache != nullptr;
+  if (has_k == cache) return hipErrorInvalidValue;  // dense Q/K/V, or q and an int8 V cache
+  if (D == 128) {
+    if (has_k)
+      prep_impl<128, true, false>(p, st);
+    else
+      prep_impl<128, false, true>(p, st);
+  } else {
+    if (has_k)
+      prep_impl<64, true, false>(p, st);
+    else
+      prep_impl<64, false, true>(p, st);
   }
   return hipGetLastError();
 }

@@ -30,6 +30,7 @@ def lib():
     L.qattn_quant_qk.argtypes = [P, I64x3, P, I64x3, I, I, I, I, I, P, P, P, P, P, P]
     L.qattn_quant_v.argtypes = [P, I64x3, I, I, I, I, P, P, P, P]
     L.qattn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P, I64x3, I, P]
+    L.qattn_prep.argtypes = [P, I64x3, P, I64x3, P, I64x3, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
     L.qattn_fwd_i8kv.argtypes = [P, I64x2, P, P, P, P, I, I, I, I, I, F, I, P, ct.c_size_t, P, I64x2, I, P]
     L.qattn_fwd_i8kv_workspace_bytes.argtypes = [I, I, I, I, I]
     L.qattn_fwd_i8kv_workspace_bytes.restype = ct.c_size_t
@@ -50,7 +51,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["qattn_quant_qk", "qattn_quant_v", "qattn_fwd", "qattn_fwd_i8kv", "qattn_fwd_i8kv_workspace_bytes",
+    for n in ["qattn_quant_qk", "qattn_quant_v", "qattn_prep", "qattn_fwd", "qattn_fwd_i8kv", "qattn_fwd_i8kv_workspace_bytes",
               "qattn_fwd_i8kv_kv_splits", "qattn_kv_append_i8", "qattn_status_string", "qattn_p8_codes"]:
         assert n in names
 
@@ -119,6 +120,32 @@ def test_quant_v_validation(lib):
     assert lib.qattn_quant_v(A, st, 1, 2, 64, 80, A, A, None, None) == EUNSUP
     assert lib.qattn_quant_v(A, st, 1, 2, 64, 64, A + 1, A, None, None) == EINVAL
     assert lib.qattn_quant_v(A, st, 1, 2, 64, 64, A, A, A + 16, None) == EINVAL  # vbf not 256-byte aligned
+
+
+def test_prep_validation(lib):
+    # the fused preparation rejects what either separate call rejects, before any launch
+    st = I64x3(1024, 128, 64)
+    ok = dict(q=A, qs=st, k=A, ks=st, v=A, vs=st, B=1, H=2, Nq=64, Nk=64, D=64, q8=A, q_scale=A, k8=A, k_scale=A,
+              k_mean=A, v8t=A, v_scale=A, vbf=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return lib.qattn_prep(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["B"], a["H"], a["Nq"], a["Nk"],
+                              a["D"], a["q8"], a["q_scale"], a["k8"], a["k_scale"], a["k_mean"], a["v8t"],
+                              a["v_scale"], a["vbf"], None)
+
+    assert call(v=None) == EINVAL
+    assert call(v8t=None) == EINVAL
+    assert call(k_mean=None) == EINVAL
+    assert call(D=96) == EUNSUP
+    assert call(Nk=0) == EINVAL
+    assert call(H=1 << 17) == EINVAL
+    assert call(v=A + 2) == EINVAL  # bf16 view not 16-byte aligned
+    assert call(vs=I64x3(1024, 129, 64)) == EINVAL  # stride not a multiple of 8 elements
+    assert call(v8t=A + 16) == EINVAL  # code buffer not 256-byte aligned
+    assert call(vbf=A + 16) == EINVAL  # vbf not 256-byte aligned
+    assert call(v_scale=A + 2) == EINVAL
 
 
 def test_fwd_validation(lib):

@@ -111,6 +111,66 @@ def test_quant_v_bit_exact(qa, B, H, Nq, Nk, D):
     assert np.array_equal(host(t["vbf"]), host(vbf_of(v8t)))  # the codes' exact bf16 values
 
 
+@pytest.mark.parametrize("B,H,Nq,Nk,D", QK_SHAPES)
+def test_prep_bit_exact(qa, B, H, Nq, Nk, D):
+    """The fused preparation (one call, four launches) against the oracle's steps 1-2."""
+    say(f"prep B={B} H={H} Nq={Nq} Nk={Nk} D={D}")
+    rng = np.random.default_rng(300 + Nq + Nk + D)
+    q = W.bf16_bits(rng.standard_normal((B, Nq, H, D)).astype(np.float32) * 3)
+    k = W.bf16_bits(rng.standard_normal((B, Nk, H, D)).astype(np.float32) + rng.uniform(-2, 2, (B, 1, H, D)).astype(np.float32))
+    v = W.bf16_bits(rng.standard_normal((B, Nk, H, D)).astype(np.float32) * np.exp2(rng.uniform(-3, 3, (1, 1, H, D))).astype(np.float32))
+    v[:, :, 0, 1] = 0  # a zero channel
+    t = qa.prep(dev_bf16(q), dev_bf16(k), dev_bf16(v))
+    torch.cuda.synchronize()
+    q8, qs, k8, ks, mean = oracle.quant_qk(q, k)
+    v8t, vs = oracle.quant_v(v)
+    assert np.array_equal(host(t["k_mean"]).view(np.uint32), mean.view(np.uint32))
+    assert np.array_equal(host(t["q8"]), q8)
+    assert np.array_equal(host(t["q_scale"]).view(np.uint32), qs.view(np.uint32))
+    assert np.array_equal(host(t["k8"]), k8)
+    assert np.array_equal(host(t["k_scale"]).view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(host(t["v8t"]), v8t)
+    assert np.array_equal(host(t["v_scale"]).view(np.uint32), vs.view(np.uint32))
+    assert np.array_equal(host(t["vbf"]), host(vbf_of(v8t)))
+
+
+def test_prep_strided_views(qa):
+    """Q, K and V as projection-strided views of one packed [B, N, 3, H, D] tensor."""
+    say("prep strided views")
+    rng = np.random.default_rng(8)
+    B, N, H, D = 2, 300, 3, 64
+    qkv = W.bf16_bits(rng.standard_normal((B, N, 3, H, D)).astype(np.float32))
+    dq = dev_bf16(qkv)
+    t = qa.prep(dq[:, :, 0], dq[:, :, 1], dq[:, :, 2])
+    torch.cuda.synchronize()
+    q8, qs, k8, ks, mean = oracle.quant_qk(qkv[:, :, 0], qkv[:, :, 1])
+    v8t, vs = oracle.quant_v(qkv[:, :, 2])
+    assert np.array_equal(host(t["q8"]), q8) and np.array_equal(host(t["k8"]), k8)
+    assert np.array_equal(host(t["k_mean"]), mean) and np.array_equal(host(t["k_scale"]), ks)
+    assert np.array_equal(host(t["q_scale"]), qs)
+    assert np.array_equal(host(t["v8t"]), v8t) and np.array_equal(host(t["v_scale"]), vs)
+
+
+def test_prep_same_bytes_as_separate_calls(qa):
+    """Identical bytes from qattn_prep and from qattn_quant_qk + qattn_quant_v, also where
+    the fp64 channel sums round (K channels mixing magnitudes 2^40 and 2^-40): both
+    paths add the same partial sums in the same order."""
+    say("prep vs separate calls")
+    rng = np.random.default_rng(11)
+    B, H, Nq, Nk, D = 1, 2, 1000, 1500, 128
+    q = W.bf16_bits(rng.standard_normal((B, Nq, H, D)).astype(np.float32))
+    kf = rng.standard_normal((B, Nk, H, D)).astype(np.float32)
+    kf *= np.exp2(rng.choice([-40.0, 0.0, 40.0], size=kf.shape)).astype(np.float32)
+    k = W.bf16_bits(kf)
+    v = W.bf16_bits(rng.standard_normal((B, Nk, H, D)).astype(np.float32))
+    dq, dk, dv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    fused = qa.prep(dq, dk, dv)
+    sep = {**qa.quant_qk(dq, dk), **qa.quant_v(dv)}
+    torch.cuda.synchronize()
+    for name in ["q8", "q_scale", "k8", "k_scale", "k_mean", "v8t", "v_scale", "vbf"]:
+        assert torch.equal(fused[name].view(torch.uint8), sep[name].view(torch.uint8)), name
+
+
 def test_quant_v_every_bf16_value(qa):
     """Channel 0 holds every bf16 value with |v| <= 448 (amax 448, so fl32(v * 1) is
     encoded as is): the GPU's e4m3 encoder must match the oracle's on all of them."""
