@@ -111,8 +111,11 @@ int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const fl
  *      (one scale per head and token: value = code * scale).
  *   workspace: >= qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D) bytes, 256-byte aligned;
  *      receives the per-channel e4m3 requantization of V (fl32(code * scale) quantized
- *      as in step 2 over all Nk tokens; its codes and their bf16 values) and the INT8
- *      blocks of q (as in step 1, no smoothing).
+ *      as in step 2 over all Nk tokens), held as the bf16 values of its codes, and the
+ *      INT8 blocks of q (as in step 1, no smoothing).  Sections, each starting on a
+ *      256-byte boundary: V scales f32 [H, D]; q codes int8 [H, Nq_pad, D]; q scales f32
+ *      [H, Nq_pad / 64]; V values bf16 [H, D, Nk_pad]; for kv_splits > 1 the partial O
+ *      f32 [S, H, Nq_pad, D] and (m, d') f32 [S, H, Nq_pad, 2].
  *   kv_splits: split-KV for few queries over a long context.  The key tiles
  *      [0, T), T = ceil(min(Nk, pos0 + Nq) / 64), are cut into kv_splits contiguous ranges
  *      [s T / S, (s + 1) T / S); each range runs the loop above on its own (from
@@ -128,9 +131,9 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
                    const int64_t out_str[2], int out_dtype, void* stream);
 
 /* Workspace size for qattn_fwd_i8kv with kv_splits key ranges (1 .. 64; resolve 0 with
- * qattn_fwd_i8kv_kv_splits first): H*D*Nk_pad (e4m3 V) + H*D*4 (V scales) + H*Nq_pad*D
- * (q codes) + H*Nq_pad/64*4 (q scales) + H*D*Nk_pad*2 (bf16 values of the V codes), and
- * for kv_splits > 1 the partial results
+ * qattn_fwd_i8kv_kv_splits first): H*D*4 (V scales) + H*Nq_pad*D (q codes) +
+ * H*Nq_pad/64*4 (q scales) + H*D*Nk_pad*2 (bf16 values of the V codes), and for
+ * kv_splits > 1 the partial results
  * kv_splits*H*Nq_pad*D*4 (O) + kv_splits*H*Nq_pad*8 (m, d'), each section rounded up to
  * 256 bytes.  Returns 0 for invalid sizes. */
 size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D, int kv_splits);

@@ -74,7 +74,8 @@ hipError_t launch_quant_v(BshdView v, const int8_t* cache, const float* tok_scal
 
 // Fused preparation (pass 1, final, pass 2, scale).  Dense form: q, k, v bf16 views with
 // k8 != nullptr; prefill form: q view (b = 0) and the int8 V cache with per-token scales,
-// k8 == nullptr.  Partial results live in the k8 and v8t regions until pass 2 writes them.
+// k8 == nullptr.  v8t or vbf may be null (not both).  Partial results live in the k8 and
+// v8t (else vbf) regions until pass 2 writes them.
 struct PrepArgs {
   BshdView q, k, v;
   int B, H, Nq, Nk;

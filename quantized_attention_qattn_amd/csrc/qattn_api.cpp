@@ -203,8 +203,8 @@ size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D, int kv_split
   if (D != 64 && D != 128) return 0;
   if (kv_splits < 1 || kv_splits > kMaxKvSplits) return 0;
   const size_t nkp = (size_t)npad64(Nk), nqp = (size_t)npad64(Nq);
-  size_t bytes = round256((size_t)H * D * nkp) + round256((size_t)H * D * 4) + round256((size_t)H * nqp * D) +
-                 round256((size_t)H * (nqp / kBlk) * 4) + round256((size_t)H * D * nkp * 2);
+  size_t bytes = round256((size_t)H * D * 4) + round256((size_t)H * nqp * D) + round256((size_t)H * (nqp / kBlk) * 4) +
+                 round256((size_t)H * D * nkp * 2);
   if (kv_splits > 1)
     bytes += round256((size_t)kv_splits * H * nqp * D * 4) + round256((size_t)kv_splits * H * nqp * 2 * 4);
   return bytes;
@@ -233,8 +233,6 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
   hipStream_t st = (hipStream_t)stream;
   const int64_t nkp = npad64(Nk), nqp = npad64(Nq);
   uint8_t* ws = (uint8_t*)workspace;
-  uint8_t* v8t = ws;
-  ws += round256((size_t)H * D * nkp);
   float* v_scale = (float*)ws;
   ws += round256((size_t)H * D * 4);
   int8_t* q8 = (int8_t*)ws;
@@ -251,8 +249,9 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
     part_md = (float*)ws;
   }
 
-  // q -> INT8 blocks (no smoothing), V cache -> per-channel e4m3 (channel-major) and its
-  // bf16 values: the fused preparation with no K
+  // q -> INT8 blocks (no smoothing), V cache -> per-channel e4m3 (channel-major), kept as
+  // the bf16 values of the codes (the only form the fused loop reads): the fused
+  // preparation with no K and no separate code array
   PrepArgs p{};
   p.q = BshdView{q, 0, q_str[0], q_str[1]};
   p.B = 1;
@@ -263,7 +262,6 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
   p.q_scale = q_scale;
   p.v_cache = v_cache;
   p.v_tok_scale = v_tok_scale;
-  p.v8t = v8t;
   p.v_scale = v_scale;
   p.vbf = vbf;
   hipError_t e = launch_prep(p, D, st);

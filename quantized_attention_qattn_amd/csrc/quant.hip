@@ -38,6 +38,9 @@ __device__ __forceinline__ void k_mean_partial_body(BshdView k, int H, int N, in
   double acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  // unrolled so that several rows' loads are in flight at once (the additions into each
+  // acc[i] stay in token order)
+#pragma unroll 4
   for (int n = n0 + rl; n < n1; n += RPP) {
     v4i w = *(const v4i*)(base + (int64_t)n * k.sn);
     float f[8];
@@ -152,47 +155,51 @@ __global__ __launch_bounds__(kThreads) void quant_i8_blocks(BshdView x, const fl
 // The input is either a bf16 view or an int8 cache with per-token scales, dequantized
 // as fl32(code * scale).
 // ---------------------------------------------------------------------------------
+// Channels per lane of the V passes: every lane moves 16 bytes per row, i.e. 8 bf16
+// channels or 16 int8 cache channels.
+template <bool CACHE>
+constexpr int v_ch() { return CACHE ? 16 : 8; }
+
 template <int D, bool CACHE>
-__device__ __forceinline__ void load_v8(BshdView v, const int8_t* cache, const float* tok_scale, int b, int h, int H,
-                                        int N, int n, int cg, float (&f)[8]) {
-  if (CACHE) {
-    const int8_t* row = cache + ((int64_t)h * N + n) * D + cg * 8;
-    uint2 w = *(const uint2*)row;
+__device__ __forceinline__ void load_v(BshdView v, const int8_t* cache, const float* tok_scale, int b, int h, int N,
+                                       int n, int cg, float (&f)[v_ch<CACHE>()]) {
+  if constexpr (CACHE) {
+    const int8_t* row = cache + ((int64_t)h * N + n) * D + cg * 16;
+    const v4i w = *(const v4i*)row;
     const float sc = tok_scale[(int64_t)h * N + n];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = (float)(int8_t)(w.x >> (8 * i)) * sc;
-      f[4 + i] = (float)(int8_t)(w.y >> (8 * i)) * sc;
-    }
+    for (int i = 0; i < 16; ++i) f[i] = (float)(int8_t)(w[i >> 2] >> (8 * (i & 3))) * sc;
   } else {
     v4i w = *(const v4i*)((const uint16_t*)v.p + b * v.sb + (int64_t)n * v.sn + h * v.sh + cg * 8);
     unpack_bf16x8(w, f);
   }
 }
 
-template <int D>
+template <int D, bool CACHE>
 struct VMaxLds {
-  float red[kThreads / (D / 8)][D];
+  float red[kThreads / (D / v_ch<CACHE>())][D];
 };
 template <int D, bool CACHE>
 __device__ __forceinline__ void v_amax_partial_body(BshdView v, const int8_t* cache, const float* tok_scale, int H,
                                                     int N, int64_t region, uint8_t* scratch, int chunk, int h, int b,
-                                                    VMaxLds<D>& lds) {
-  constexpr int CPR = D / 8, RPP = kThreads / CPR;
+                                                    VMaxLds<D, CACHE>& lds) {
+  constexpr int CH = v_ch<CACHE>(), CPR = D / CH, RPP = kThreads / CPR;
   auto& red = lds.red;
   const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
   const int n0 = chunk * kChunk, n1 = min(N, n0 + kChunk);
-  float mx[8];
+  float mx[CH];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) mx[i] = 0.0f;
+  for (int i = 0; i < CH; ++i) mx[i] = 0.0f;
+  // unrolled so that several rows' loads are in flight at once
+#pragma unroll 4
   for (int n = n0 + rl; n < n1; n += RPP) {
-    float f[8];
-    load_v8<D, CACHE>(v, cache, tok_scale, b, h, H, N, n, cg, f);
+    float f[CH];
+    load_v<D, CACHE>(v, cache, tok_scale, b, h, N, n, cg, f);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mx[i] = fmaxf(mx[i], fabsf(f[i]));
+    for (int i = 0; i < CH; ++i) mx[i] = fmaxf(mx[i], fabsf(f[i]));
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) red[rl][cg * 8 + i] = mx[i];
+  for (int i = 0; i < CH; ++i) red[rl][cg * CH + i] = mx[i];
   __syncthreads();
   if (t < D) {
     float m = 0.0f;
@@ -204,7 +211,7 @@ __device__ __forceinline__ void v_amax_partial_body(BshdView v, const int8_t* ca
 template <int D, bool CACHE>
 __global__ __launch_bounds__(kThreads) void v_amax_partial(BshdView v, const int8_t* cache, const float* tok_scale,
                                                            int H, int N, int64_t region, uint8_t* scratch) {
-  __shared__ VMaxLds<D> lds;
+  __shared__ VMaxLds<D, CACHE> lds;
   v_amax_partial_body<D, CACHE>(v, cache, tok_scale, H, N, region, scratch, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
@@ -231,38 +238,39 @@ template <int D, bool CACHE>
 __device__ __forceinline__ void v_encode_body(BshdView v, const int8_t* cache, const float* tok_scale, int H, int N,
                                               int npad, const float* v_amax, uint8_t* v8t, uint16_t* vbf, int tile,
                                               int h, int b, VEncLds<D>& lds) {
-  constexpr int CPR = D / 8, RPP = kThreads / CPR, PASSES = kBlk / RPP;
+  constexpr int CH = v_ch<CACHE>(), CPR = D / CH, RPP = kThreads / CPR, PASSES = kBlk / RPP;
+  static_assert(PASSES >= 1 && RPP * PASSES == kBlk, "one 64-token tile per workgroup");
   constexpr int PITCH = kEncPitch;
   uint8_t* sT = lds.sT;
   const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
   const int64_t bh = (int64_t)b * H + h;
   const int n0 = tile * kBlk;
-  float rc[8];
-  bool zc[8];
+  float rc[CH];
+  bool zc[CH];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = v_amax[bh * D + cg * 8 + i];
+  for (int i = 0; i < CH; ++i) {
+    const float a = v_amax[bh * D + cg * CH + i];
     zc[i] = !(a > 0.0f);
     rc[i] = zc[i] ? 0.0f : fminf(448.0f / a, kFltMax);
   }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int nl = rl + p * RPP, n = n0 + nl;
-    float f[8];
+    float f[CH];
     if (n < N) {
-      load_v8<D, CACHE>(v, cache, tok_scale, b, h, H, N, n, cg, f);
+      load_v<D, CACHE>(v, cache, tok_scale, b, h, N, n, cg, f);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+      for (int i = 0; i < CH; ++i) f[i] = 0.0f;
     }
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
+    for (int i = 0; i < CH; i += 2) {
       // hardware e4m3 conversion: round to nearest even; |f * r| <= 448 (1 + 2^-23)
       uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[i] * rc[i], f[i + 1] * rc[i + 1], 0, false);
       uint32_t c0 = (zc[i] || n >= N) ? 0u : (w & 0xffu);
       uint32_t c1 = (zc[i + 1] || n >= N) ? 0u : ((w >> 8) & 0xffu);
-      sT[(cg * 8 + i) * PITCH + nl] = (uint8_t)c0;
-      sT[(cg * 8 + i + 1) * PITCH + nl] = (uint8_t)c1;
+      sT[(cg * CH + i) * PITCH + nl] = (uint8_t)c0;
+      sT[(cg * CH + i + 1) * PITCH + nl] = (uint8_t)c1;
     }
   }
   __syncthreads();
@@ -270,7 +278,7 @@ __device__ __forceinline__ void v_encode_body(BshdView v, const int8_t* cache, c
   for (int id = t; id < CHUNKS; id += kThreads) {
     const int c = id >> 2, part = id & 3;
     const v4i w = *(const v4i*)(sT + c * PITCH + 16 * part);
-    *(v4i*)(v8t + (bh * D + c) * npad + n0 + 16 * part) = w;
+    if (v8t) *(v4i*)(v8t + (bh * D + c) * npad + n0 + 16 * part) = w;
     if (vbf) {  // the exact bf16 values of the 16 codes (every e4m3 value is a bf16 value)
       uint32_t b[8];
 #pragma unroll
@@ -315,11 +323,11 @@ template <int D, bool HAS_K, bool CACHE>
 __global__ __launch_bounds__(kThreads) void prep_pass1(BshdView q, int Nq, int nqpad, int8_t* q8, float* q_scale,
                                                        BshdView k, BshdView v, const int8_t* v_cache,
                                                        const float* v_tok_scale, int H, int Nk, int64_t region,
-                                                       int8_t* k_part, uint8_t* v_part) {
+                                                       int8_t* k_part, int64_t v_region, uint8_t* v_part) {
   constexpr int QB = kChunk / kBlk;  // Q blocks per chunk
   __shared__ float wmax[QB][kThreads / 64];
   __shared__ KSumLds<D> klds;
-  __shared__ VMaxLds<D> vlds;
+  __shared__ VMaxLds<D, CACHE> vlds;
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   if (q8) {
 #pragma unroll
@@ -330,16 +338,17 @@ __global__ __launch_bounds__(kThreads) void prep_pass1(BshdView q, int Nq, int n
   }
   if (chunk < nchunks(Nk)) {
     if (HAS_K) k_mean_partial_body<D>(k, H, Nk, region, k_part, chunk, h, b, klds);
-    v_amax_partial_body<D, CACHE>(v, v_cache, v_tok_scale, H, Nk, region, v_part, chunk, h, b, vlds);
+    v_amax_partial_body<D, CACHE>(v, v_cache, v_tok_scale, H, Nk, v_region, v_part, chunk, h, b, vlds);
   }
 }
 
 template <int D, bool HAS_K>
 __global__ __launch_bounds__(D) void prep_final(int Nk, int nchunk, int64_t region, const int8_t* k_part,
-                                                float* k_mean, const uint8_t* v_part, float* v_amax) {
+                                                float* k_mean, int64_t v_region, const uint8_t* v_part,
+                                                float* v_amax) {
   const int bh = blockIdx.x, c = threadIdx.x;
   if (HAS_K) k_mean[(int64_t)bh * D + c] = k_mean_of_chunks<D>((const double*)(k_part + bh * region), nchunk, Nk, c);
-  v_amax[(int64_t)bh * D + c] = v_amax_of_chunks<D>((const float*)(v_part + bh * region), nchunk, c);
+  v_amax[(int64_t)bh * D + c] = v_amax_of_chunks<D>((const float*)(v_part + bh * v_region), nchunk, c);
 }
 
 template <int D, bool HAS_K, bool CACHE>
@@ -358,11 +367,15 @@ template <int D, bool HAS_K, bool CACHE>
 static void prep_impl(const PrepArgs& p, hipStream_t st) {
   const int nqp = p.q8 ? (p.Nq + kBlk - 1) / kBlk * kBlk : 0;
   const int nkp = (p.Nk + kBlk - 1) / kBlk * kBlk;
-  const int64_t region = (int64_t)nkp * D;  // bytes of k8 and of v8t per (b, h): partial-result scratch
+  // partial results live in the output buffers of pass 2 (per (b, h): k8 holds nkp * D
+  // bytes; v8t nkp * D, or vbf 2 * nkp * D where there is no v8t)
+  const int64_t region = (int64_t)nkp * D;
+  const int64_t v_region = p.v8t ? region : 2 * region;
+  uint8_t* v_part = p.v8t ? p.v8t : (uint8_t*)p.vbf;
   const int nck = nchunks(p.Nk), ncq = p.q8 ? nchunks(p.Nq) : 0;
   prep_pass1<D, HAS_K, CACHE><<<dim3(max(nck, ncq), p.H, p.B), kThreads, 0, st>>>(
-      p.q, p.Nq, nqp, p.q8, p.q_scale, p.k, p.v, p.v_cache, p.v_tok_scale, p.H, p.Nk, region, p.k8, p.v8t);
-  prep_final<D, HAS_K><<<p.B * p.H, D, 0, st>>>(p.Nk, nck, region, p.k8, p.k_mean, p.v8t, p.v_scale);
+      p.q, p.Nq, nqp, p.q8, p.q_scale, p.k, p.v, p.v_cache, p.v_tok_scale, p.H, p.Nk, region, p.k8, v_region, v_part);
+  prep_final<D, HAS_K><<<p.B * p.H, D, 0, st>>>(p.Nk, nck, region, p.k8, p.k_mean, v_region, v_part, p.v_scale);
   prep_pass2<D, HAS_K, CACHE><<<dim3(nkp / kBlk, p.H, p.B), kThreads, 0, st>>>(
       p.k, p.k_mean, p.k8, p.k_scale, p.v, p.v_cache, p.v_tok_scale, p.v_scale, p.v8t, p.vbf, p.H, p.Nk, nkp);
   const int64_t n = (int64_t)p.B * p.H * D;
@@ -490,6 +503,7 @@ hipError_t launch_quant_v(BshdView v, const int8_t* cache, const float* tok_scal
 hipError_t launch_prep(const PrepArgs& p, int D, hipStream_t st) {
   const bool has_k = p.k8 != nullptr, cache = p.v_cache != nullptr;
   if (has_k == cache) return hipErrorInvalidValue;  // dense Q/K/V, or q and an int8 V cache
+  if (!p.v8t && !p.vbf) return hipErrorInvalidValue;
   if (D == 128) {
     if (has_k)
       prep_impl<128, true, false>(p, st);

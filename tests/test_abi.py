@@ -68,13 +68,13 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # H*D*Nk_pad + H*D*4 + H*Nq_pad*D + H*Nq_pad/64*4 + H*D*Nk_pad*2, each rounded up to 256 bytes
+    # H*D*4 + H*Nq_pad*D + H*Nq_pad/64*4 + H*D*Nk_pad*2, each rounded up to 256 bytes
     H, Nq, Nk, D = 32, 1024, 32768, 128
-    expect = H * D * Nk + H * D * 4 + H * Nq * D + ((H * Nq // 64 * 4 + 255) // 256) * 256 + H * D * Nk * 2
+    expect = H * D * 4 + H * Nq * D + ((H * Nq // 64 * 4 + 255) // 256) * 256 + H * D * Nk * 2
     assert lib.qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, 1) == expect
     # split-KV adds S*H*Nq_pad*D*4 (partial O) + S*H*Nq_pad*8 (m, d')
     assert lib.qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, 4) == expect + 4 * H * Nq * D * 4 + 4 * H * Nq * 8
-    assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 64, 1) == 2 * 64 * 64 + 512 + 2 * 64 * 64 + 256 + 2 * 64 * 64 * 2
+    assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 64, 1) == 512 + 2 * 64 * 64 + 256 + 2 * 64 * 64 * 2
     assert lib.qattn_fwd_i8kv_workspace_bytes(0, 1, 1, 64, 1) == 0
     assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 96, 1) == 0
     assert lib.qattn_fwd_i8kv_workspace_bytes(2, 1, 1, 64, 0) == 0

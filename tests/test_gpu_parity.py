@@ -223,6 +223,19 @@ def vbf_of(v8t: np.ndarray) -> torch.Tensor:
     return dev_bf16(W.bf16_bits(dec[v8t]))
 
 
+def i8kv_workspace(wsh: np.ndarray, H: int, Nq: int, Nk: int, D: int) -> dict:
+    """The sections of a qattn_fwd_i8kv workspace (host copy), as the header lays them out."""
+    nqp, nkp = oracle.npad(Nq), oracle.npad(Nk)
+    r = lambda n: (n + 255) // 256 * 256
+    out, off = {}, 0
+    for name, nbytes, dt, shape in [("v_scale", H * D * 4, np.float32, (H, D)), ("q8", H * nqp * D, np.int8, (H, nqp, D)),
+                                    ("q_scale", H * (nqp // 64) * 4, np.float32, (H, nqp // 64)),
+                                    ("vbf", H * D * nkp * 2, np.uint16, (H, D, nkp))]:
+        out[name] = wsh[off: off + nbytes].view(dt).reshape(shape)
+        off += r(nbytes)
+    return out
+
+
 def run_fwd(qa, ops, Nq, Nk, lam, causal, out_dtype=torch.float32):
     q8, qs, k8, ks, vs = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (ops[0], ops[1], ops[2], ops[3], ops[5])]
     vbf = vbf_of(np.ascontiguousarray(ops[4]))
@@ -345,13 +358,10 @@ def test_i8kv_small(qa):
         torch.cuda.synchronize()
         S = qa.qattn_fwd_i8kv_kv_splits(H, Nq, Nk, pos0)
         ref, it = oracle.fwd_i8kv(q, kc, kts, vc, vts, pos0, kv_splits=S)
-        wsh = host(ws)
-        nkp, nqp = oracle.npad(Nk), oracle.npad(Nq)
-        assert np.array_equal(wsh[: H * D * nkp].reshape(H, D, nkp), it["v8t"])
-        off = (H * D * nkp + 255) // 256 * 256
-        assert np.array_equal(wsh[off: off + H * D * 4].view(np.float32).reshape(H, D), it["v_scale"])
-        off += (H * D * 4 + 255) // 256 * 256
-        assert np.array_equal(wsh[off: off + H * nqp * D].view(np.int8).reshape(H, nqp, D), it["q8"])
+        sec = i8kv_workspace(host(ws), H, Nq, Nk, D)
+        assert np.array_equal(sec["v_scale"], it["v_scale"])
+        assert np.array_equal(sec["q8"], it["q8"])
+        assert np.array_equal(sec["vbf"], host(vbf_of(it["v8t"])))  # the V codes, bit for bit
         assert_close(host(out), ref, f"i8kv H={H} Nq={Nq} Nk={Nk} pos0={pos0}")
 
 
@@ -578,9 +588,11 @@ def test_i8kv_workload_full_size(qa, name):
     say("  oracle requant + quant")
     v8t, vsc = oracle.requant_v_cache(vc, vts)
     q8, qs = oracle.quant_i8_blocks(q[None])
-    wsh = host(ws)
-    H, D, nkp = w.H, w.D, oracle.npad(w.Nk)
-    assert np.array_equal(wsh[: H * D * nkp].reshape(H, D, nkp), v8t)
+    H, D = w.H, w.D
+    sec = i8kv_workspace(host(ws), H, w.Nq, w.Nk, D)
+    assert np.array_equal(sec["vbf"], host(vbf_of(v8t)))  # the V codes, bit for bit
+    assert np.array_equal(sec["v_scale"], vsc) and np.array_equal(sec["q8"], q8[0])
+    assert np.array_equal(sec["q_scale"].view(np.uint32), qs[0].view(np.uint32))
     rng = np.random.default_rng(11)
     rows = _sample_rows(w.Nq, rng, nblk=2)
     heads = sorted(set([0, w.H - 1, int(rng.integers(w.H))]))
