@@ -507,11 +507,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     // The MFMA phase has one branch-free form: the first one runs PV on a zeroed V^T
     // buffer with P = 0, the last one computes a QK that nobody reads, and a wave whose
     // rows see no key of the tile has P = 0 (separate forms would make the compiler copy
-    // the O accumulators between register sets every iteration).  The LDS reads are
-    // issued ahead of the MFMAs that consume them: the K fragments and the first half of
-    // the V^T codes before the QK MFMAs, the second half once the K fragments are
-    // consumed (register budget).  The PV MFMAs run chunk-major, so consecutive MFMAs
-    // accumulate into different O blocks.
+    // the O accumulators between register sets every iteration).
     const uint8_t* tK = sK[buf];
     const uint8_t* tV = sVb[buf];  // bf16 V^T of tile i - 1
     // lane (channel row, half hh) reads the bf16 V^T of keys 32 hh + 8 c .. + 7 of its row
@@ -519,47 +515,58 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
       const int vrow = 32 * s + l32;
       return *(const v8bf*)(tV + vrow * (2 * BN) + 16 * ((4 * hh + c) ^ vbswz(vrow)));
     };
-    auto pv_step = [&](int c, const v8bf* vfrag) {
-      const v8bf pfrag = __builtin_bit_cast(v8bf, v4i{(int)pb[4 * c], (int)pb[4 * c + 1], (int)pb[4 * c + 2],
-                                                      (int)pb[4 * c + 3]});
-#pragma unroll
-      for (int s = 0; s < NS; ++s) O[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag[s], pfrag, O[s], 0, 0, 0);
+    // The phase is a pipeline of 2 NS QK steps and 4 NS PV steps; step k reads one
+    // 16-byte operand from LDS and runs one MFMA on it.  Operands are read kPrefetch steps
+    // ahead into a ring of registers, so that every read's latency hides behind the
+    // MFMAs before its own.  QK steps alternate the two score blocks; PV steps run
+    // chunk-major (each O block accumulates its four key chunks in order, as before).
+    constexpr int kQkSteps = 2 * NS, kSteps = kQkSteps + 4 * NS, kPrefetch = 4;
+    auto read_op = [&](auto k_c) -> v4i {
+      constexpr int k = decltype(k_c)::value;
+      if constexpr (k < kQkSteps) {
+        const int krow = (k & 1) ? krow1 : krow0;
+        const int ch = NS * hh + k / 2;
+        return *(const v4i*)(tK + krow * D + 16 * (ch ^ kswz<D>(krow)));
+      } else {
+        return __builtin_bit_cast(v4i, read_v((k - kQkSteps) % NS, (k - kQkSteps) / NS));
+      }
+    };
+    auto mfma_op = [&](auto k_c, const v4i& op) {
+      constexpr int k = decltype(k_c)::value;
+      if constexpr (k < kQkSteps) {
+        if constexpr (k & 1)
+          S1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(op, qf[k / 2], S1, 0, 0, 0);
+        else
+          S0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(op, qf[k / 2], S0, 0, 0, 0);
+      } else {
+        constexpr int c = (k - kQkSteps) / NS, s = (k - kQkSteps) % NS;
+        const v8bf pfrag = __builtin_bit_cast(v8bf, v4i{(int)pb[4 * c], (int)pb[4 * c + 1], (int)pb[4 * c + 2],
+                                                        (int)pb[4 * c + 3]});
+        O[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, op), pfrag, O[s], 0, 0, 0);
+      }
     };
     {
-      v4i kf[2 * NS];
-      v8bf vf0[NS], vf1[NS];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int ch = NS * hh + s;
-        kf[2 * s] = *(const v4i*)(tK + krow0 * D + 16 * (ch ^ kswz<D>(krow0)));
-        kf[2 * s + 1] = *(const v4i*)(tK + krow1 * D + 16 * (ch ^ kswz<D>(krow1)));
-      }
-#pragma unroll
-      for (int s = 0; s < NS; ++s) vf0[s] = read_v(s, 0);
+      v4i ring[kPrefetch];
+      static_for<kPrefetch>([&](auto k_c) { ring[decltype(k_c)::value] = read_op(k_c); });
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         S0[r] = kAccBias;
         S1[r] = kAccBias;
       }
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        S0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[2 * s], qf[s], S0, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[2 * s + 1], qf[s], S1, 0, 0, 0);
-      }
-      // every LDS read of this block ahead of the QK MFMAs (the scheduler would
-      // otherwise place each read right before its MFMA and expose its latency)
-      __builtin_amdgcn_sched_group_barrier(0x100, 3 * NS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NS, 0);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) vf1[s] = read_v(s, 1);
-      pv_step(0, vf0);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) vf0[s] = read_v(s, 2);
-      pv_step(1, vf1);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) vf1[s] = read_v(s, 3);
-      pv_step(2, vf0);
-      pv_step(3, vf1);
+      static_for<kSteps>([&](auto k_c) {
+        constexpr int k = decltype(k_c)::value;
+        const v4i op = ring[k % kPrefetch];
+        if constexpr (k + kPrefetch < kSteps) ring[k % kPrefetch] = read_op(std::integral_constant<int, k + kPrefetch>{});
+        mfma_op(k_c, op);
+      });
+      // pin that order: the first reads, then each MFMA followed by the read kPrefetch
+      // steps ahead (left alone, the scheduler places most reads right before their MFMA
+      // and waits out each latency)
+      __builtin_amdgcn_sched_group_barrier(0x100, kPrefetch, 0);
+      static_for<kSteps>([&](auto k_c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (decltype(k_c)::value + kPrefetch < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      });
     }
     phase_barrier();
 
