@@ -151,7 +151,8 @@ __global__ __launch_bounds__(kThreads) void quant_i8_blocks(BshdView x, const fl
 // ---------------------------------------------------------------------------------
 // a3: per-channel e4m3 V.  Pass 1: per-chunk channel absmax into scratch inside v8t;
 // pass 2: the channel absmax is parked in v_scale; pass 3: encode 64-token tiles and
-// write them channel-major through an LDS transpose; pass 4: v_scale = absmax / 448.
+// write them channel-major (each lane codes eight tokens of its channels, so no transpose
+// buffer is needed); pass 4: v_scale = absmax / 448.
 // The input is either a bf16 view or an int8 cache with per-token scales, dequantized
 // as fl32(code * scale).
 // ---------------------------------------------------------------------------------
@@ -229,74 +230,81 @@ __global__ __launch_bounds__(D) void v_amax_final(int nchunk, int64_t region, co
   v_scale[(int64_t)bh * D + c] = v_amax_of_chunks<D>((const float*)(scratch + (int64_t)bh * region), nchunk, c);
 }
 
-constexpr int kEncPitch = kBlk + 16;  // V transpose buffer row pitch (bytes)
-template <int D>
-struct VEncLds {
-  __align__(16) uint8_t sT[D * kEncPitch];
-};
+// Encode of one 64-token tile, channel-major, without a transpose buffer: lane L of the
+// tile owns tokens 8 o .. 8 o + 7 (o = L % 8) of the channel group g = L / 8 (CH
+// channels).  It loads its 8 rows, then forms each channel's codes four tokens to a word
+// (the e4m3 conversion takes any two values: tokens t, t + 1 into the low half of the
+// word, t + 2, t + 3 into the high half), so the codes come out in the order they are
+// stored.  Eight lanes of a group store 64 contiguous bytes of codes and 128 of bf16
+// values per channel.  Lanes L >= kEncLanes do nothing.
 template <int D, bool CACHE>
-__device__ __forceinline__ void v_encode_body(BshdView v, const int8_t* cache, const float* tok_scale, int H, int N,
+constexpr int enc_lanes() { return 8 * (D / v_ch<CACHE>()); }
+
+template <int D, bool CACHE>
+__device__ __forceinline__ void v_encode_tile(BshdView v, const int8_t* cache, const float* tok_scale, int H, int N,
                                               int npad, const float* v_amax, uint8_t* v8t, uint16_t* vbf, int tile,
-                                              int h, int b, VEncLds<D>& lds) {
-  constexpr int CH = v_ch<CACHE>(), CPR = D / CH, RPP = kThreads / CPR, PASSES = kBlk / RPP;
-  static_assert(PASSES >= 1 && RPP * PASSES == kBlk, "one 64-token tile per workgroup");
-  constexpr int PITCH = kEncPitch;
-  uint8_t* sT = lds.sT;
-  const int t = threadIdx.x, cg = t % CPR, rl = t / CPR;
+                                              int h, int b, int L) {
+  constexpr int CH = v_ch<CACHE>();
+  if (L >= enc_lanes<D, CACHE>()) return;
+  const int o = L & 7, g = L >> 3;
   const int64_t bh = (int64_t)b * H + h;
-  const int n0 = tile * kBlk;
+  const int n0 = tile * kBlk + 8 * o;  // this lane's first token
   float rc[CH];
   bool zc[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const float a = v_amax[bh * D + cg * CH + i];
+    const float a = v_amax[bh * D + g * CH + i];
     zc[i] = !(a > 0.0f);
     rc[i] = zc[i] ? 0.0f : fminf(448.0f / a, kFltMax);
   }
+  uint32_t cw[2][CH];  // [token quad][channel]: the codes of four tokens of one channel
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int nl = rl + p * RPP, n = n0 + nl;
-    float f[CH];
-    if (n < N) {
-      load_v<D, CACHE>(v, cache, tok_scale, b, h, N, n, cg, f);
-    } else {
+  for (int hq = 0; hq < 2; ++hq) {
+    float f[4][CH];
 #pragma unroll
-      for (int i = 0; i < CH; ++i) f[i] = 0.0f;
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + 4 * hq + r;
+      if (n < N) {
+        load_v<D, CACHE>(v, cache, tok_scale, b, h, N, n, g, f[r]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) f[r][i] = 0.0f;  // padding tokens: code 0x00
+      }
     }
 #pragma unroll
-    for (int i = 0; i < CH; i += 2) {
+    for (int i = 0; i < CH; ++i) {
       // hardware e4m3 conversion: round to nearest even; |f * r| <= 448 (1 + 2^-23)
-      uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[i] * rc[i], f[i + 1] * rc[i + 1], 0, false);
-      uint32_t c0 = (zc[i] || n >= N) ? 0u : (w & 0xffu);
-      uint32_t c1 = (zc[i + 1] || n >= N) ? 0u : ((w >> 8) & 0xffu);
-      sT[(cg * CH + i) * PITCH + nl] = (uint8_t)c0;
-      sT[(cg * CH + i + 1) * PITCH + nl] = (uint8_t)c1;
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[0][i] * rc[i], f[1][i] * rc[i], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(f[2][i] * rc[i], f[3][i] * rc[i], w, true);
+      cw[hq][i] = zc[i] ? 0u : (uint32_t)w;  // a zero channel codes as 0x00 (also for -0)
     }
   }
-  __syncthreads();
-  constexpr int CHUNKS = D * (kBlk / 16);
-  for (int id = t; id < CHUNKS; id += kThreads) {
-    const int c = id >> 2, part = id & 3;
-    const v4i w = *(const v4i*)(sT + c * PITCH + 16 * part);
-    if (v8t) *(v4i*)(v8t + (bh * D + c) * npad + n0 + 16 * part) = w;
-    if (vbf) {  // the exact bf16 values of the 16 codes (every e4m3 value is a bf16 value)
-      uint32_t b[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        b[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, false));
-        b[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[e], 1.0f, true));
+  for (int i = 0; i < CH; ++i) {
+    const int64_t row = (bh * D + g * CH + i) * npad + tile * kBlk + 8 * o;
+    if (v8t) *(uint2*)(v8t + row) = make_uint2(cw[0][i], cw[1][i]);
+    if (vbf) {  // the exact bf16 values of the 8 codes (every e4m3 value is a bf16 value)
+      uint32_t bw[4];
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq) {
+        bw[2 * hq] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hq][i], 1.0f, false));
+        bw[2 * hq + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[hq][i], 1.0f, true));
       }
-      uint16_t* dst = vbf + (bh * D + c) * npad + n0 + 16 * part;
-      *(v4i*)dst = v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-      *(v4i*)(dst + 8) = v4i{(int)b[4], (int)b[5], (int)b[6], (int)b[7]};
+      *(v4i*)(vbf + row) = v4i{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3]};
     }
   }
 }
+// Tiles per 256-thread workgroup of the standalone encode launches.
+template <int D, bool CACHE>
+constexpr int enc_tiles_per_wg() { return kThreads / enc_lanes<D, CACHE>(); }
+
 template <int D, bool CACHE>
 __global__ __launch_bounds__(kThreads) void v_encode(BshdView v, const int8_t* cache, const float* tok_scale, int H,
                                                      int N, int npad, const float* v_amax, uint8_t* v8t, uint16_t* vbf) {
-  __shared__ VEncLds<D> lds;
-  v_encode_body<D, CACHE>(v, cache, tok_scale, H, N, npad, v_amax, v8t, vbf, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+  constexpr int TPW = enc_tiles_per_wg<D, CACHE>(), EL = enc_lanes<D, CACHE>();
+  const int t = threadIdx.x, tile = blockIdx.x * TPW + t / EL;
+  if (tile < npad / kBlk)
+    v_encode_tile<D, CACHE>(v, cache, tok_scale, H, N, npad, v_amax, v8t, vbf, tile, blockIdx.y, blockIdx.z, t % EL);
 }
 
 __global__ void v_scale_from_amax(float* v_scale, int64_t n) {
@@ -351,16 +359,26 @@ __global__ __launch_bounds__(D) void prep_final(int Nk, int nchunk, int64_t regi
   v_amax[(int64_t)bh * D + c] = v_amax_of_chunks<D>((const float*)(v_part + bh * v_region), nchunk, c);
 }
 
+// pass 2: blocks [0, nkt) of the dense form code one K block each (all 256 threads);
+// the blocks after them encode enc_tiles_per_wg V tiles each
 template <int D, bool HAS_K, bool CACHE>
 __global__ __launch_bounds__(kThreads) void prep_pass2(BshdView k, const float* k_mean, int8_t* k8, float* k_scale,
                                                        BshdView v, const int8_t* v_cache, const float* v_tok_scale,
                                                        const float* v_amax, uint8_t* v8t, uint16_t* vbf, int H,
                                                        int Nk, int nkpad) {
+  constexpr int TPW = enc_tiles_per_wg<D, CACHE>(), EL = enc_lanes<D, CACHE>();
   __shared__ float wmax[kThreads / 64];
-  __shared__ VEncLds<D> elds;
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  if (HAS_K) quant_i8_block_body<D, true>(k, k_mean, H, Nk, nkpad, k8, k_scale, tile, h, b, wmax);
-  v_encode_body<D, CACHE>(v, v_cache, v_tok_scale, H, Nk, nkpad, v_amax, v8t, vbf, tile, h, b, elds);
+  const int t = threadIdx.x, h = blockIdx.y, b = blockIdx.z, nkt = nkpad / kBlk;
+  int vb = blockIdx.x;
+  if (HAS_K) {
+    if (vb < nkt) {  // uniform over the workgroup: the barrier inside is safe
+      quant_i8_block_body<D, true>(k, k_mean, H, Nk, nkpad, k8, k_scale, vb, h, b, wmax);
+      return;
+    }
+    vb -= nkt;
+  }
+  const int tile = vb * TPW + t / EL;
+  if (tile < nkt) v_encode_tile<D, CACHE>(v, v_cache, v_tok_scale, H, Nk, nkpad, v_amax, v8t, vbf, tile, h, b, t % EL);
 }
 
 template <int D, bool HAS_K, bool CACHE>
@@ -376,7 +394,9 @@ static void prep_impl(const PrepArgs& p, hipStream_t st) {
   prep_pass1<D, HAS_K, CACHE><<<dim3(max(nck, ncq), p.H, p.B), kThreads, 0, st>>>(
       p.q, p.Nq, nqp, p.q8, p.q_scale, p.k, p.v, p.v_cache, p.v_tok_scale, p.H, p.Nk, region, p.k8, v_region, v_part);
   prep_final<D, HAS_K><<<p.B * p.H, D, 0, st>>>(p.Nk, nck, region, p.k8, p.k_mean, v_region, v_part, p.v_scale);
-  prep_pass2<D, HAS_K, CACHE><<<dim3(nkp / kBlk, p.H, p.B), kThreads, 0, st>>>(
+  constexpr int TPW = enc_tiles_per_wg<D, CACHE>();
+  const int nkt = nkp / kBlk, nb2 = (HAS_K ? nkt : 0) + (nkt + TPW - 1) / TPW;
+  prep_pass2<D, HAS_K, CACHE><<<dim3(nb2, p.H, p.B), kThreads, 0, st>>>(
       p.k, p.k_mean, p.k8, p.k_scale, p.v, p.v_cache, p.v_tok_scale, p.v_scale, p.v8t, p.vbf, p.H, p.Nk, nkp);
   const int64_t n = (int64_t)p.B * p.H * D;
   v_scale_from_amax<<<(int)((n + 255) / 256), 256, 0, st>>>(p.v_scale, n);
@@ -479,7 +499,9 @@ static void quant_v_impl(BshdView v, const int8_t* cache, const float* tok_scale
   const int nc = nchunks(N);
   v_amax_partial<D, CACHE><<<dim3(nc, H, B), kThreads, 0, st>>>(v, cache, tok_scale, H, N, region, v8t);
   v_amax_final<D><<<B * H, D, 0, st>>>(nc, region, v8t, v_scale);
-  v_encode<D, CACHE><<<dim3(npad / kBlk, H, B), kThreads, 0, st>>>(v, cache, tok_scale, H, N, npad, v_scale, v8t, vbf);
+  constexpr int TPW = enc_tiles_per_wg<D, CACHE>();
+  v_encode<D, CACHE><<<dim3((npad / kBlk + TPW - 1) / TPW, H, B), kThreads, 0, st>>>(v, cache, tok_scale, H, N, npad,
+                                                                                    v_scale, v8t, vbf);
   const int64_t n = (int64_t)B * H * D;
   v_scale_from_amax<<<(int)((n + 255) / 256), 256, 0, st>>>(v_scale, n);
 }
