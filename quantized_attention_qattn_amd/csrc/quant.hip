@@ -64,19 +64,33 @@ __global__ __launch_bounds__(kThreads) void k_mean_partial(BshdView k, int H, in
   k_mean_partial_body<D>(k, H, N, region, scratch, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
-// channel c of one (b, h): the chunk sums added in chunk order (the loop is unrolled so
-// that the loads are issued ahead of the dependent additions)
+// The final reductions run kFinalThreads threads per (b, h): kFinalThreads / D per
+// channel.  Thread j of channel c folds chunks j, j + J, j + 2 J, ... in that order, then
+// the J partial results are folded in j order through LDS: a fixed order, shared by the
+// separate and the fused preparation.
+constexpr int kFinalThreads = 1024;
 template <int D>
-__device__ __forceinline__ float k_mean_of_chunks(const double* part, int nchunk, int N, int c) {
+__device__ __forceinline__ void k_mean_of_chunks(const double* part, int nchunk, int N, double* red, float* mean) {
+  constexpr int J = kFinalThreads / D;
+  const int c = threadIdx.x % D, j = threadIdx.x / D;
   double s = 0.0;
-#pragma unroll 8
-  for (int i = 0; i < nchunk; ++i) s += part[i * D + c];
-  return (float)(s / (double)N);
+#pragma unroll 4
+  for (int i = j; i < nchunk; i += J) s += part[i * D + c];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (j == 0) {
+    double t = red[c];
+#pragma unroll
+    for (int r = 1; r < J; ++r) t += red[r * D + c];
+    mean[c] = (float)(t / (double)N);
+  }
 }
 template <int D>
-__global__ __launch_bounds__(D) void k_mean_final(int N, int nchunk, int64_t region, const int8_t* scratch, float* mean) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  mean[(int64_t)bh * D + c] = k_mean_of_chunks<D>((const double*)(scratch + (int64_t)bh * region), nchunk, N, c);
+__global__ __launch_bounds__(kFinalThreads) void k_mean_final(int N, int nchunk, int64_t region, const int8_t* scratch,
+                                                              float* mean) {
+  __shared__ double red[kFinalThreads];
+  const int bh = blockIdx.x;
+  k_mean_of_chunks<D>((const double*)(scratch + (int64_t)bh * region), nchunk, N, red, mean + (int64_t)bh * D);
 }
 
 // ---------------------------------------------------------------------------------
@@ -217,17 +231,28 @@ __global__ __launch_bounds__(kThreads) void v_amax_partial(BshdView v, const int
 }
 
 template <int D>
-__device__ __forceinline__ float v_amax_of_chunks(const float* part, int nchunk, int c) {
+__device__ __forceinline__ void v_amax_of_chunks(const float* part, int nchunk, float* red, float* amax) {
+  constexpr int J = kFinalThreads / D;
+  const int c = threadIdx.x % D, j = threadIdx.x / D;
   float m = 0.0f;
-#pragma unroll 8
-  for (int i = 0; i < nchunk; ++i) m = fmaxf(m, part[i * D + c]);
-  return m;
+#pragma unroll 4
+  for (int i = j; i < nchunk; i += J) m = fmaxf(m, part[i * D + c]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  if (j == 0) {
+    float t = red[c];
+#pragma unroll
+    for (int r = 1; r < J; ++r) t = fmaxf(t, red[r * D + c]);
+    amax[c] = t;
+  }
 }
 template <int D>
-__global__ __launch_bounds__(D) void v_amax_final(int nchunk, int64_t region, const uint8_t* scratch, float* v_scale) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+__global__ __launch_bounds__(kFinalThreads) void v_amax_final(int nchunk, int64_t region, const uint8_t* scratch,
+                                                              float* v_scale) {
+  __shared__ float red[kFinalThreads];
+  const int bh = blockIdx.x;
   // the absmax; converted to the scale after encoding
-  v_scale[(int64_t)bh * D + c] = v_amax_of_chunks<D>((const float*)(scratch + (int64_t)bh * region), nchunk, c);
+  v_amax_of_chunks<D>((const float*)(scratch + (int64_t)bh * region), nchunk, red, v_scale + (int64_t)bh * D);
 }
 
 // Encode of one 64-token tile, channel-major, without a transpose buffer: lane L of the
@@ -351,12 +376,14 @@ __global__ __launch_bounds__(kThreads) void prep_pass1(BshdView q, int Nq, int n
 }
 
 template <int D, bool HAS_K>
-__global__ __launch_bounds__(D) void prep_final(int Nk, int nchunk, int64_t region, const int8_t* k_part,
-                                                float* k_mean, int64_t v_region, const uint8_t* v_part,
-                                                float* v_amax) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  if (HAS_K) k_mean[(int64_t)bh * D + c] = k_mean_of_chunks<D>((const double*)(k_part + bh * region), nchunk, Nk, c);
-  v_amax[(int64_t)bh * D + c] = v_amax_of_chunks<D>((const float*)(v_part + bh * v_region), nchunk, c);
+__global__ __launch_bounds__(kFinalThreads) void prep_final(int Nk, int nchunk, int64_t region, const int8_t* k_part,
+                                                            float* k_mean, int64_t v_region, const uint8_t* v_part,
+                                                            float* v_amax) {
+  __shared__ double kred[kFinalThreads];
+  __shared__ float vred[kFinalThreads];
+  const int bh = blockIdx.x;
+  if (HAS_K) k_mean_of_chunks<D>((const double*)(k_part + bh * region), nchunk, Nk, kred, k_mean + (int64_t)bh * D);
+  v_amax_of_chunks<D>((const float*)(v_part + bh * v_region), nchunk, vred, v_amax + (int64_t)bh * D);
 }
 
 // pass 2: blocks [0, nkt) of the dense form code one K block each (all 256 threads);
@@ -393,7 +420,8 @@ static void prep_impl(const PrepArgs& p, hipStream_t st) {
   const int nck = nchunks(p.Nk), ncq = p.q8 ? nchunks(p.Nq) : 0;
   prep_pass1<D, HAS_K, CACHE><<<dim3(max(nck, ncq), p.H, p.B), kThreads, 0, st>>>(
       p.q, p.Nq, nqp, p.q8, p.q_scale, p.k, p.v, p.v_cache, p.v_tok_scale, p.H, p.Nk, region, p.k8, v_region, v_part);
-  prep_final<D, HAS_K><<<p.B * p.H, D, 0, st>>>(p.Nk, nck, region, p.k8, p.k_mean, v_region, v_part, p.v_scale);
+  prep_final<D, HAS_K><<<p.B * p.H, kFinalThreads, 0, st>>>(p.Nk, nck, region, p.k8, p.k_mean, v_region, v_part,
+                                                             p.v_scale);
   constexpr int TPW = enc_tiles_per_wg<D, CACHE>();
   const int nkt = nkp / kBlk, nb2 = (HAS_K ? nkt : 0) + (nkt + TPW - 1) / TPW;
   prep_pass2<D, HAS_K, CACHE><<<dim3(nb2, p.H, p.B), kThreads, 0, st>>>(
@@ -412,10 +440,10 @@ hipError_t launch_k_mean(BshdView k, int B, int H, int N, int D, int npad, int8_
   dim3 g1(nc, H, B);
   if (D == 128) {
     k_mean_partial<128><<<g1, kThreads, 0, st>>>(k, H, N, region, scratch);
-    k_mean_final<128><<<B * H, 128, 0, st>>>(N, nc, region, scratch, mean);
+    k_mean_final<128><<<B * H, kFinalThreads, 0, st>>>(N, nc, region, scratch, mean);
   } else {
     k_mean_partial<64><<<g1, kThreads, 0, st>>>(k, H, N, region, scratch);
-    k_mean_final<64><<<B * H, 64, 0, st>>>(N, nc, region, scratch, mean);
+    k_mean_final<64><<<B * H, kFinalThreads, 0, st>>>(N, nc, region, scratch, mean);
   }
   return hipGetLastError();
 }
@@ -498,7 +526,7 @@ static void quant_v_impl(BshdView v, const int8_t* cache, const float* tok_scale
   const int64_t region = (int64_t)npad * D;  // bytes of v8t per (b, h)
   const int nc = nchunks(N);
   v_amax_partial<D, CACHE><<<dim3(nc, H, B), kThreads, 0, st>>>(v, cache, tok_scale, H, N, region, v8t);
-  v_amax_final<D><<<B * H, D, 0, st>>>(nc, region, v8t, v_scale);
+  v_amax_final<D><<<B * H, kFinalThreads, 0, st>>>(nc, region, v8t, v_scale);
   constexpr int TPW = enc_tiles_per_wg<D, CACHE>();
   v_encode<D, CACHE><<<dim3((npad / kBlk + TPW - 1) / TPW, H, B), kThreads, 0, st>>>(v, cache, tok_scale, H, N, npad,
                                                                                     v_scale, v8t, vbf);
