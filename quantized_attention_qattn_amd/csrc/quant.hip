@@ -282,25 +282,41 @@ __device__ __forceinline__ void v_encode_tile(BshdView v, const int8_t* cache, c
     zc[i] = !(a > 0.0f);
     rc[i] = zc[i] ? 0.0f : fminf(448.0f / a, kFltMax);
   }
+  // all eight rows' loads first (raw 16-byte words, and the token scales of a cache),
+  // then each channel decoded from them: every load is in flight at once
+  v4i raw[8];
+  float sc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int n = n0 + r;
+    raw[r] = v4i{0, 0, 0, 0};  // padding tokens: value 0, code 0x00
+    sc[r] = 0.0f;
+    if (n < N) {
+      if constexpr (CACHE) {
+        raw[r] = *(const v4i*)(cache + ((int64_t)h * N + n) * D + g * 16);
+        sc[r] = tok_scale[(int64_t)h * N + n];
+      } else {
+        raw[r] = *(const v4i*)((const uint16_t*)v.p + b * v.sb + (int64_t)n * v.sn + h * v.sh + g * 8);
+      }
+    }
+  }
+  // channel i of row r: fl32(code * scale) for a cache, the bf16 value otherwise
+  auto value = [&](int r, int i) -> float {
+    if constexpr (CACHE) {
+      return (float)(int8_t)(raw[r][i >> 2] >> (8 * (i & 3))) * sc[r];
+    } else {
+      const uint32_t w = (uint32_t)raw[r][i >> 1];
+      return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+  };
   uint32_t cw[2][CH];  // [token quad][channel]: the codes of four tokens of one channel
 #pragma unroll
   for (int hq = 0; hq < 2; ++hq) {
-    float f[4][CH];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = n0 + 4 * hq + r;
-      if (n < N) {
-        load_v<D, CACHE>(v, cache, tok_scale, b, h, N, n, g, f[r]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) f[r][i] = 0.0f;  // padding tokens: code 0x00
-      }
-    }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       // hardware e4m3 conversion: round to nearest even; |f * r| <= 448 (1 + 2^-23)
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(f[0][i] * rc[i], f[1][i] * rc[i], 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(f[2][i] * rc[i], f[3][i] * rc[i], w, true);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(value(4 * hq, i) * rc[i], value(4 * hq + 1, i) * rc[i], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(value(4 * hq + 2, i) * rc[i], value(4 * hq + 3, i) * rc[i], w, true);
       cw[hq][i] = zc[i] ? 0u : (uint32_t)w;  // a zero channel codes as 0x00 (also for -0)
     }
   }
