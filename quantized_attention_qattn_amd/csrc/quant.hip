@@ -175,18 +175,30 @@ __global__ __launch_bounds__(kThreads) void quant_i8_blocks(BshdView x, const fl
 template <bool CACHE>
 constexpr int v_ch() { return CACHE ? 16 : 8; }
 
+// Row n of V for channel group cg as raw words: 16 bytes, and (cache) the token's scale;
+// padding rows (n >= N) read as zeros.  value_of decodes channel i: fl32(code * scale)
+// for a cache, the bf16 value otherwise.
 template <int D, bool CACHE>
-__device__ __forceinline__ void load_v(BshdView v, const int8_t* cache, const float* tok_scale, int b, int h, int N,
-                                       int n, int cg, float (&f)[v_ch<CACHE>()]) {
+__device__ __forceinline__ void load_v_raw(BshdView v, const int8_t* cache, const float* tok_scale, int b, int h,
+                                           int N, int n, int cg, v4i& raw, float& sc) {
+  raw = v4i{0, 0, 0, 0};
+  sc = 0.0f;
+  if (n < N) {
+    if constexpr (CACHE) {
+      raw = *(const v4i*)(cache + ((int64_t)h * N + n) * D + cg * 16);
+      sc = tok_scale[(int64_t)h * N + n];
+    } else {
+      raw = *(const v4i*)((const uint16_t*)v.p + b * v.sb + (int64_t)n * v.sn + h * v.sh + cg * 8);
+    }
+  }
+}
+template <bool CACHE>
+__device__ __forceinline__ float value_of(const v4i& raw, float sc, int i) {
   if constexpr (CACHE) {
-    const int8_t* row = cache + ((int64_t)h * N + n) * D + cg * 16;
-    const v4i w = *(const v4i*)row;
-    const float sc = tok_scale[(int64_t)h * N + n];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) f[i] = (float)(int8_t)(w[i >> 2] >> (8 * (i & 3))) * sc;
+    return (float)(int8_t)(raw[i >> 2] >> (8 * (i & 3))) * sc;  // fl32(code * scale)
   } else {
-    v4i w = *(const v4i*)((const uint16_t*)v.p + b * v.sb + (int64_t)n * v.sn + h * v.sh + cg * 8);
-    unpack_bf16x8(w, f);
+    const uint32_t w = (uint32_t)raw[i >> 1];
+    return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
   }
 }
 
@@ -208,10 +220,11 @@ __device__ __forceinline__ void v_amax_partial_body(BshdView v, const int8_t* ca
   // unrolled so that several rows' loads are in flight at once
 #pragma unroll 4
   for (int n = n0 + rl; n < n1; n += RPP) {
-    float f[CH];
-    load_v<D, CACHE>(v, cache, tok_scale, b, h, N, n, cg, f);
+    v4i raw;
+    float sc;
+    load_v_raw<D, CACHE>(v, cache, tok_scale, b, h, N, n, cg, raw, sc);
 #pragma unroll
-    for (int i = 0; i < CH; ++i) mx[i] = fmaxf(mx[i], fabsf(f[i]));
+    for (int i = 0; i < CH; ++i) mx[i] = fmaxf(mx[i], fabsf(value_of<CACHE>(raw, sc, i)));
   }
 #pragma unroll
   for (int i = 0; i < CH; ++i) red[rl][cg * CH + i] = mx[i];
@@ -287,28 +300,8 @@ __device__ __forceinline__ void v_encode_tile(BshdView v, const int8_t* cache, c
   v4i raw[8];
   float sc[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int n = n0 + r;
-    raw[r] = v4i{0, 0, 0, 0};  // padding tokens: value 0, code 0x00
-    sc[r] = 0.0f;
-    if (n < N) {
-      if constexpr (CACHE) {
-        raw[r] = *(const v4i*)(cache + ((int64_t)h * N + n) * D + g * 16);
-        sc[r] = tok_scale[(int64_t)h * N + n];
-      } else {
-        raw[r] = *(const v4i*)((const uint16_t*)v.p + b * v.sb + (int64_t)n * v.sn + h * v.sh + g * 8);
-      }
-    }
-  }
-  // channel i of row r: fl32(code * scale) for a cache, the bf16 value otherwise
-  auto value = [&](int r, int i) -> float {
-    if constexpr (CACHE) {
-      return (float)(int8_t)(raw[r][i >> 2] >> (8 * (i & 3))) * sc[r];
-    } else {
-      const uint32_t w = (uint32_t)raw[r][i >> 1];
-      return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
-    }
-  };
+  for (int r = 0; r < 8; ++r) load_v_raw<D, CACHE>(v, cache, tok_scale, b, h, N, n0 + r, g, raw[r], sc[r]);
+  auto value = [&](int r, int i) { return value_of<CACHE>(raw[r], sc[r], i); };
   uint32_t cw[2][CH];  // [token quad][channel]: the codes of four tokens of one channel
 #pragma unroll
   for (int hq = 0; hq < 2; ++hq) {
