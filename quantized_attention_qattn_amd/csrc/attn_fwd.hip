@@ -10,9 +10,9 @@
 //   * a workgroup owns 256 query rows of one (b, h): 8 waves x 32 rows.  Waves w and
 //     w + 4 share a SIMD.  Each wave alternates an MFMA phase (QK of tile i and PV of
 //     tile i - 1) with a VALU phase (online softmax of tile i); group 1 (waves 4-7) runs
-//     one phase behind group 0, so while one wave of a SIMD issues matrix instructions its
-//     partner is in the softmax.  (Measured on MI355X: a wave that interleaves both kinds
-//     of work in its own instruction stream overlaps them far less.)
+//     one phase behind group 0, so the two waves of a SIMD start each interval in
+//     different kinds of phase and one issues matrix instructions while its partner is in
+//     the softmax;
 //   * scores are computed transposed, S^T = K . Q^T, with v_mfma_i32_32x32x32_i8: the
 //     accumulator gives each lane one query (its column) and 32 keys of the tile (16 per
 //     32-key block), so the row max and row sum are in-lane plus one exchange with the
@@ -32,12 +32,14 @@
 //   * workgroups are mapped so each XCD walks one contiguous range of (b, h, query block)
 //     and keeps the K/V it streams in its own L2.
 //
-// Tile pipeline (tick k = the interval between two workgroup barriers; group 0 runs
-// phase k of its sequence M0 V0 M1 V1 ..., group 1 phase k - 1):
-//   slot j = {K tile j, bf16 V^T of tile j - 1} sits in buffer j % 3.  Group 0 issues
-//   the loads of slot j at the start of its VALU phase j - 2 (tick 2j - 3) and waits for
-//   them at the end of its VALU phase j - 1 (tick 2j - 1).  The MFMA phases j read slot
-//   j at ticks 2j (group 0) and 2j + 1 (group 1); the buffer is reloaded at tick 2j + 3.
+// Tile pipeline: interval i (between two workgroup barriers) holds group 0's MFMA phase i
+// and VALU phase i, and group 1's VALU phase i - 1 and MFMA phase i.
+//   slot j = {K tile j, bf16 V^T of tile j - 1} sits in buffer j % 3.  Both groups' MFMA
+//   phases j read it in interval j.  Group 0 issues its loads at the start of interval
+//   j - 2 (the buffer's previous slot, j - 3, was read in interval j - 3) and waits for
+//   them at the end of interval j - 1.  The per-key scales of a per-token cache follow
+//   the same ring (sC[j % 3]): group 1 reads those of tile j in interval j + 1, before
+//   group 0 overwrites them at the end of interval j + 2.
 #include <climits>
 #include <type_traits>
 #include <utility>
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   constexpr int QB = BM / kBlk;     // 64-row Q scale blocks per workgroup
   __shared__ __align__(16) uint8_t sK[NBUF][BN * D];   // K codes, swizzled for the QK reads
   __shared__ __align__(16) uint8_t sVb[NBUF][D * BN * 2];  // bf16 V^T of each slot, swizzled
-  __shared__ __align__(16) float sC[2][QB][BN];     // PER_TOKEN: c_j per (buffer, query block, key)
+  __shared__ __align__(16) float sC[NBUF][QB][BN];  // PER_TOKEN: c_j per (buffer, query block, key)
   __shared__ __align__(16) float sKs[NBUF][BN];     // PER_TOKEN: raw K scales of each slot
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(PT + (PER_TOKEN ? 1 : 0)));
   };
   auto scale_store = [&](int t, int buf) {  // c of slot t (buffer buf), after its wait
-    if (PER_TOKEN) sC[t & 1][gtid >> 6][gtid & (BN - 1)] = (sq_mine * sKs[buf][gtid & (BN - 1)]) * a.lambda;
+    if (PER_TOKEN) sC[buf][gtid >> 6][gtid & (BN - 1)] = (sq_mine * sKs[buf][gtid & (BN - 1)]) * a.lambda;
   };
   float m = -INFINITY;  // running max (log2 domain)
   float dsum = 0.0f;    // this lane's share of d'' = 2^80 d' (its 32 keys of every tile)
@@ -496,10 +498,10 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
       (const __attribute__((address_space(4))) float*)uniform_ptr(a.k_scale + bh * a.ks_bh);
   const int nkb = (a.Nk + BN - 1) / BN;  // K scale blocks
   float ks_next = (!PER_TOKEN && ntiles > 0) ? ks_const[t0] : 0.0f;
-  if (grp == 1) phase_barrier();
-  // One iteration of the tile loop for slot i, which sits in buffer BUF = i % NBUF.  The
-  // loop is unrolled NBUF times so that the buffer offsets of every LDS access are
-  // immediates: the per-lane addresses stay in registers and no iteration recomputes them.
+  // One interval of the tile loop (between two workgroup barriers) for slot i, which sits
+  // in buffer BUF = i % NBUF.  The loop is unrolled NBUF times so that the buffer offsets
+  // of every LDS access are immediates: the per-lane addresses stay in registers and no
+  // interval recomputes them.
   auto iteration = [&](const int i, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
     constexpr int buf1 = (buf + 1) % NBUF, buf2 = (buf + 2) % NBUF;
@@ -508,6 +510,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     // buffer with P = 0, the last one computes a QK that nobody reads, and a wave whose
     // rows see no key of the tile has P = 0 (separate forms would make the compiler copy
     // the O accumulators between register sets every iteration).
+    auto mfma_phase = [&]() {
     const uint8_t* tK = sK[buf];
     const uint8_t* tV = sVb[buf];  // bf16 V^T of tile i - 1
     // lane (channel row, half hh) reads the bf16 V^T of keys 32 hh + 8 c .. + 7 of its row
@@ -568,22 +571,22 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
         if constexpr (decltype(k_c)::value + kPrefetch < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       });
     }
-    phase_barrier();
+    };
 
-    // ---- VALU phase i: online softmax of tile i ----
-    if (grp == 0 && i + 2 <= ntiles) stage(i + 2, std::integral_constant<int, buf2>{});
+    // ---- VALU phase j: online softmax of tile j (its per-key scales in sC[jbuf]) ----
+    auto valu_phase = [&](const int j, const int jbuf) {
     // per-tile K scale of this tile (loaded during the previous VALU phase) and of the
     // next one: uniform addresses read through the constant address space, i.e. scalar
     // loads, issued a phase ahead so that their latency is never waited for
     const float ks_cur = ks_next;
-    if (!PER_TOKEN && t0 + i + 1 < nkb) ks_next = ks_const[t0 + i + 1];
-    if (i < wtiles) {
-      const int ti = t0 + i;  // absolute tile
+    if (!PER_TOKEN && t0 + j + 1 < nkb) ks_next = ks_const[t0 + j + 1];
+    if (j < wtiles) {
+      const int ti = t0 + j;  // absolute tile
       const int key0 = ti * BN + 32 * hh;
       const bool masked =
           (ti * BN + BN > a.Nk) || (CAUSAL && (int64_t)ti * BN + BN - 1 > (int64_t)qw + a.pos_off);
       const float c_tile = PER_TOKEN ? 0.0f : (sq_w * ks_cur) * a.lambda;
-      const float* cp = &sC[i & 1][wave >> 1][32 * hh];
+      const float* cp = &sC[jbuf][wave >> 1][32 * hh];
       float alpha;
       v8i pf;
       const float m_old = m;
@@ -603,9 +606,21 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
       for (int w = 0; w < 8; ++w) fp8x4_to_bf16(pf[w], pb[2 * w], pb[2 * w + 1]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) pb[j] = 0u;  // no contribution from this tile
+      for (int w = 0; w < 16; ++w) pb[w] = 0u;  // no contribution from this tile
     }
-    // group 0: slot i + 1 (issued three ticks back) must have landed before the MFMA
+    };
+
+    // Group 0 runs MFMA phase i, then the softmax of tile i; group 1 the softmax of tile
+    // i - 1, then MFMA phase i.  So the two waves of a SIMD start the interval in
+    // different kinds of phase, and each wave's softmax of tile j precedes its MFMA
+    // phase j + 1, which needs the P of tile j.
+    if (grp == 0 && i + 2 <= ntiles) stage(i + 2, std::integral_constant<int, buf2>{});
+    if (grp == 0) mfma_phase();
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 0 || i >= 1) valu_phase(grp == 0 ? i : i - 1, grp == 0 ? buf : buf2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 1) mfma_phase();
+    // group 0: slot i + 1 (issued one interval back) must have landed before the MFMA
     // phases i + 1 read it; its raw K scales give the c of tile i + 1
     if (grp == 0 && i < ntiles) {
       wait_all_but(i + 2);
@@ -622,7 +637,6 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     iteration(i, std::integral_constant<int, 2>{});
     if (++i > ntiles) break;
   }
-  if (grp == 0) phase_barrier();
 
   // ---- epilogue: out = O * s_v / d' ----
   const float dt = sum_with_partner(dsum) * kPScaleInv;  // d' = d'' / 2^80, exact
