@@ -71,10 +71,11 @@ __device__ __forceinline__ float p_from_u(float u) { return __builtin_amdgcn_exp
 typedef short v2s_t __attribute__((ext_vector_type(2)));
 
 // e4m3 codes of P' = P'' / 2^80 for four values (bytes 0..3).  Both halves of the word
-// are written, so the first conversion may start from any register (here a's bits)
-// instead of a zeroed one.
-__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  v2s_t w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s_t, a), a, b, kPScale, false);
+// are written, so the first conversion may start from any register: `spent` is a value
+// that has no other use, whose register the result then takes over in place (a value
+// still needed later would cost a copy, a zeroed start a move).
+__device__ __forceinline__ int pack_fp8x4(float spent, float a, float b, float c, float d) {
+  v2s_t w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s_t, spent), a, b, kPScale, false);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, kPScale, true);
   return __builtin_bit_cast(int, w);
 }
@@ -229,13 +230,14 @@ __device__ __forceinline__ int select_visible_or_zero(int x, int lim) {
   return x;
 }
 
-// Online-softmax update of one 64-key tile for this lane's query and its 32 keys
+// Online-softmax step of one 64-key tile for this lane's query and its 32 keys
 // (key0 + i, i = 16 kb + j held in S_kb[j]).  Returns the 32 FP8 codes of P' = 256 P
-// packed as the B operand of the PV MFMA; updates m, the lane's share of d'' = 2^80 d',
-// and alpha.
+// packed as the B operand of the PV MFMA; updates m and returns in `tsum` the lane's
+// share of the tile's sum of P'' = 2^80 P' (the caller folds it into d'' with the
+// factor alpha of the old terms).
 template <bool MASKED, bool PER_TOKEN>
 __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, const float* cp, float c_tile,
-                                            int key0, int vis_last, float& m, float& dsum, float& alpha) {
+                                            int key0, int vis_last, float& m, float& tsum) {
   float cvec[32];
   if (PER_TOKEN) {
 #pragma unroll
@@ -282,29 +284,33 @@ __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, cons
       mxb = max(max(mxb, am[16 + i]), am[16 + i + 1]);
     }
     const int mx = max_with_partner(max(mxa, mxb));
-    Mt = mx <= 0 ? -INFINITY : acc_f32(mx) * c_tile;  // <= 0: every key of the row hidden
+    // a visible key's biased accumulator is positive, so a maximum of 0 means that every
+    // key of the row is hidden, which only a masked tile can have
+    Mt = (MASKED && mx <= 0) ? -INFINITY : acc_f32(mx) * c_tile;
   }
   const float mnew = fmaxf(m, Mt);
-  const float ms = mnew == -INFINITY ? 0.0f : mnew;
-  alpha = mnew == m ? 1.0f : __builtin_amdgcn_exp2f(m - ms);
+  // m stays -inf while every key so far is hidden (masked tiles only: an unmasked
+  // tile's maximum is finite)
+  const float ms = (MASKED && mnew == -INFINITY) ? 0.0f : mnew;
   const float bconst = 88.0f - ms;  // u = S - m + 88: P' = 2^(u - 80) peaks at 2^8
   m = mnew;
   // four partial sums keep the additions off one dependent chain (the order of the
   // additions into d' is not part of the contract; the result is an fp32 sum of P'',
   // i.e. 2^80 times an fp32 sum of P')
-  float ds[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float ds[4];
   v8i pf;
-  float p[32];
+  float p[32], u0[8];
   static_for<32>([&](auto i_c) {
     constexpr int i = decltype(i_c)::value;
     float u = __builtin_fmaf(acc_f32(accv[i]), PER_TOKEN ? cvec[i] : c_tile, bconst);
     if (MASKED) u = __builtin_bit_cast(float, select_visible<i>(__builtin_bit_cast(int, u), lim, ninf));
     p[i] = p_from_u(u);
-    ds[i & 3] += p[i];
+    if (i % 4 == 0) u0[i / 4] = u;
+    ds[i & 3] = i < 4 ? p[i] : ds[i & 3] + p[i];
   });
 #pragma unroll
-  for (int w = 0; w < 8; ++w) pf[w] = pack_fp8x4(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3]);
-  dsum = dsum * alpha + ((ds[0] + ds[1]) + (ds[2] + ds[3]));
+  for (int w = 0; w < 8; ++w) pf[w] = pack_fp8x4(u0[w], p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3]);
+  tsum = (ds[0] + ds[1]) + (ds[2] + ds[3]);
   return pf;
 }
 
@@ -473,6 +479,15 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[s][r] = 0.0f;
   v16i S0, S1;
+  // With per-block K scales the first QK MFMA of each score block reads its start value
+  // (the accumulator bias) from this register vector, set once; the empty asm makes it
+  // opaque, so the compiler does not rebuild it every tile.  With per-token scales (32
+  // more values per lane in registers) there is no room for it: the MFMA phase resets
+  // the accumulators instead.
+  v16i bias16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bias16[r] = kAccBias;
+  if constexpr (!PER_TOKEN) asm volatile("" : "+v"(bias16));
   uint32_t pb[16];  // bf16 P of the last softmax: keys 32 hh + 2 j, 2 j + 1 in word j
 #pragma unroll
   for (int j = 0; j < 16; ++j) pb[j] = 0u;
@@ -537,10 +552,11 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     auto mfma_op = [&](auto k_c, const v4i& op) {
       constexpr int k = decltype(k_c)::value;
       if constexpr (k < kQkSteps) {
+        constexpr bool first = !PER_TOKEN && k < 2;
         if constexpr (k & 1)
-          S1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(op, qf[k / 2], S1, 0, 0, 0);
+          S1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(op, qf[k / 2], first ? bias16 : S1, 0, 0, 0);
         else
-          S0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(op, qf[k / 2], S0, 0, 0, 0);
+          S0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(op, qf[k / 2], first ? bias16 : S0, 0, 0, 0);
       } else {
         constexpr int c = (k - kQkSteps) / NS, s = (k - kQkSteps) % NS;
         const v8bf pfrag = __builtin_bit_cast(v8bf, v4i{(int)pb[4 * c], (int)pb[4 * c + 1], (int)pb[4 * c + 2],
@@ -551,10 +567,12 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     {
       v4i ring[kPrefetch];
       static_for<kPrefetch>([&](auto k_c) { ring[decltype(k_c)::value] = read_op(k_c); });
+      if constexpr (PER_TOKEN) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        S0[r] = kAccBias;
-        S1[r] = kAccBias;
+        for (int r = 0; r < 16; ++r) {
+          S0[r] = kAccBias;
+          S1[r] = kAccBias;
+        }
       }
       static_for<kSteps>([&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
@@ -587,20 +605,27 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
           (ti * BN + BN > a.Nk) || (CAUSAL && (int64_t)ti * BN + BN - 1 > (int64_t)qw + a.pos_off);
       const float c_tile = PER_TOKEN ? 0.0f : (sq_w * ks_cur) * a.lambda;
       const float* cp = &sC[jbuf][wave >> 1][32 * hh];
-      float alpha;
+      float tsum;
       v8i pf;
       const float m_old = m;
       if (masked) {
         const int vis_last = (int)min(CAUSAL ? (int64_t)qrow + a.pos_off : (int64_t)a.Nk - 1, (int64_t)a.Nk - 1);
-        pf = softmax_tile<true, PER_TOKEN>(S0, S1, cp, c_tile, key0, vis_last, m, dsum, alpha);
+        pf = softmax_tile<true, PER_TOKEN>(S0, S1, cp, c_tile, key0, vis_last, m, tsum);
       } else {
-        pf = softmax_tile<false, PER_TOKEN>(S0, S1, cp, c_tile, key0, 0, m, dsum, alpha);
+        pf = softmax_tile<false, PER_TOKEN>(S0, S1, cp, c_tile, key0, 0, m, tsum);
       }
+      // alpha = 2^(m_old - m) rescales the old terms of d'' and O; it is exactly 1 for a
+      // row whose maximum stayed (d'' * 1 = d''), so the exponential, the product and the
+      // rescale run only when some row of the wave has a new maximum (then m is finite)
       if (__ballot(m != m_old) != 0) {
+        const float alpha = m == m_old ? 1.0f : __builtin_amdgcn_exp2f(m_old - m);
+        dsum = dsum * alpha + tsum;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
           for (int r = 0; r < 16; ++r) O[s][r] *= alpha;
+      } else {
+        dsum = dsum + tsum;
       }
 #pragma unroll
       for (int w = 0; w < 8; ++w) fp8x4_to_bf16(pf[w], pb[2 * w], pb[2 * w + 1]);
