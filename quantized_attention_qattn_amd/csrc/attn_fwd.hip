@@ -35,11 +35,18 @@
 // Tile pipeline: interval i (between two workgroup barriers) holds group 0's MFMA phase i
 // and VALU phase i, and group 1's VALU phase i - 1 and MFMA phase i.
 //   slot j = {K tile j, bf16 V^T of tile j - 1} sits in buffer j % 3.  Both groups' MFMA
-//   phases j read it in interval j.  Group 0 issues its loads at the start of interval
-//   j - 2 (the buffer's previous slot, j - 3, was read in interval j - 3) and waits for
-//   them at the end of interval j - 1.  The per-key scales of a per-token cache follow
-//   the same ring (sC[j % 3]): group 1 reads those of tile j in interval j + 1, before
-//   group 0 overwrites them at the end of interval j + 2.
+//   phases j read it in interval j.  Group 1, which finishes its interval earlier, issues
+//   the loads at the start of interval j - 2 (the buffer's previous slot, j - 3, was read
+//   in interval j - 3) and waits for them at the end of interval j - 1.  The per-key
+//   scales of a per-token cache follow the same ring (sC[j % 3]): the groups read those of
+//   tile j in intervals j and j + 1, before group 1 overwrites them at the end of
+//   interval j + 2.
+//
+// Issue priority: of a SIMD's two waves the hardware favours the older one, group 0, and
+// group 1's softmax then advances little while group 0 issues.  So each wave raises its
+// priority (s_setprio) for its MFMA phase (2: an MFMA issues as soon as the matrix core
+// is free) and group 1 for its softmax (1), which then ends in time for group 1's MFMA
+// phase to run beside group 0's softmax (0).
 #include <climits>
 #include <type_traits>
 #include <utility>
@@ -350,7 +357,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
-  const int grp = wave >> 2;  // group 0 loads the tiles and leads by one phase
+  const int grp = wave >> 2;  // group 0 leads by one phase; group 1 loads the tiles
   const int gtid = tid & 255;  // thread index within the group
   const int l32 = lane & 31, hh = lane >> 5;
   const int nqb = (a.Nq + BM - 1) / BM;
@@ -382,9 +389,9 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     for (int s = 0; s < NS; ++s) qf[s] = v4i{0, 0, 0, 0};
   }
   const float sq_w = wave_live ? a.q_scale[bh * a.qs_bh + qw / kBlk] : 0.0f;
-  // group 0 thread t computes c for query block t / 64 and key t % 64 of each tile
+  // group 1 thread t computes c for query block t / 64 and key t % 64 of each tile
   float sq_mine = 0.0f;
-  if (PER_TOKEN && grp == 0 && q0 + kBlk * (gtid >> 6) < a.nq_pad)
+  if (PER_TOKEN && grp == 1 && q0 + kBlk * (gtid >> 6) < a.nq_pad)
     sq_mine = a.q_scale[bh * a.qs_bh + q0 / kBlk + (gtid >> 6)];
 
   // tiles streamed by the workgroup, and tiles holding a key visible to this wave
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   wtiles = __builtin_amdgcn_readfirstlane(max(0, min(wtiles, t_end) - t0));
 
   // ---- staging: global -> LDS directly (buffer loads with the LDS destination) ----
-  // Each group-0 wave fills PT 1 KiB segments of the K tile and PTV of the bf16 V^T tile;
+  // Each group-1 wave fills PT 1 KiB segments of the K tile and PTV of the bf16 V^T tile;
   // lane l of a segment writes LDS slot 64 seg + l (16 bytes), so each lane fetches the
   // global chunk that the swizzled layout keeps in that slot.
   // Buffer resources are per (b, h) with 32-bit offsets; rows past the end of the
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     voff[i] = row * (int)(2 * a.ldv) + 16 * q;
   }
   // Slot t: K tile t and its raw per-token K scales (t < ntiles), and the bf16 V^T of
-  // tile t - 1 (t >= 1), into buffer buf = t % NBUF.  Every group-0 wave loads all 64
+  // tile t - 1 (t >= 1), into buffer buf = t % NBUF.  Every group-1 wave loads all 64
   // raw scales of the tile itself (the waves write identical bytes), so that its own
   // wait makes them visible to it.  All slot traffic goes through the direct-to-LDS
   // loads: a compiler-visible load whose value is used while tile loads are in flight
@@ -500,7 +507,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   // compiler's waits for them, placed inside the loop, would also wait for the tile
   // loads in flight
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
-  if (grp == 0 && ntiles > 0) {
+  if (grp == 1 && ntiles > 0) {
     stage(0, std::integral_constant<int, 0>{});
     stage(1, std::integral_constant<int, 1>{});
     wait_all_but(1);
@@ -638,16 +645,26 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
     // Group 0 runs MFMA phase i, then the softmax of tile i; group 1 the softmax of tile
     // i - 1, then MFMA phase i.  So the two waves of a SIMD start the interval in
     // different kinds of phase, and each wave's softmax of tile j precedes its MFMA
-    // phase j + 1, which needs the P of tile j.
-    if (grp == 0 && i + 2 <= ntiles) stage(i + 2, std::integral_constant<int, buf2>{});
-    if (grp == 0) mfma_phase();
+    // phase j + 1, which needs the P of tile j.  The priorities are those of the header.
+    if (grp == 1 && i + 2 <= ntiles) stage(i + 2, std::integral_constant<int, buf2>{});
+    if (grp == 0) {
+      __builtin_amdgcn_s_setprio(2);
+      mfma_phase();
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+      __builtin_amdgcn_s_setprio(1);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (grp == 0 || i >= 1) valu_phase(grp == 0 ? i : i - 1, grp == 0 ? buf : buf2);
     __builtin_amdgcn_sched_barrier(0);
-    if (grp == 1) mfma_phase();
-    // group 0: slot i + 1 (issued one interval back) must have landed before the MFMA
+    if (grp == 1) {
+      __builtin_amdgcn_s_setprio(2);
+      mfma_phase();
+      __builtin_amdgcn_s_setprio(0);
+    }
+    // group 1: slot i + 1 (issued one interval back) must have landed before the MFMA
     // phases i + 1 read it; its raw K scales give the c of tile i + 1
-    if (grp == 0 && i < ntiles) {
+    if (grp == 1 && i < ntiles) {
       wait_all_but(i + 2);
       if (i + 1 < ntiles) scale_store(i + 1, buf1);
     }
