@@ -81,9 +81,10 @@ int qattn_quant_v(const void* v, const int64_t v_str[3], int B, int H, int Nk, i
  * kernels): the outputs of qattn_quant_qk followed by qattn_quant_v, byte for byte, from
  * four launches instead of eight.  Q is read once; K and V twice (the channel mean and
  * the channel absmax need every token before any token is coded).  Arguments, layouts
- * and alignment are those of the two calls; vbf may be NULL.  k8 and v8t hold partial
- * results during the call.  Returns QATTN_EINVAL / QATTN_EUNSUPPORTED before any launch
- * on a bad argument. */
+ * and alignment are those of the two calls; either v8t or vbf (not both) may be NULL,
+ * so a caller that runs qattn_fwd only needs vbf.  k8, and v8t (or vbf when v8t is
+ * NULL), hold partial results during the call.  Returns QATTN_EINVAL /
+ * QATTN_EUNSUPPORTED before any launch on a bad argument. */
 int qattn_prep(const void* q, const int64_t q_str[3], const void* k, const int64_t k_str[3], const void* v,
                const int64_t v_str[3], int B, int H, int Nq, int Nk, int D, int8_t* q8, float* q_scale, int8_t* k8,
                float* k_scale, float* k_mean, uint8_t* v8t, float* v_scale, uint16_t* vbf, void* stream);
@@ -98,18 +99,24 @@ int qattn_prep(const void* q, const int64_t q_str[3], const void* k, const int64
  *   causal: key j visible to query i iff j <= i + (Nk - Nq) (bottom-right aligned); a
  *           query with no visible key outputs zeros.
  *   out: [B, Nq, H, D] view with strides out_str, dtype out_dtype (token-major NHD).
- * Output = fl32(O * s_v / d') with fp32 accumulation; bf16 output is its RNE rounding. */
+ * Output = fl32(O * s_v / d') with fp32 accumulation; bf16 output is its RNE rounding.
+ * Score domain: every finite input whose log2-domain scores S = acc * c stay below 2^28
+ * in magnitude, including the P codes that saturate at 448 once |S| reaches about 2^22
+ * (the oracle's encoder saturates the same way).  Beyond 2^28 the fp32 sum d' itself may
+ * overflow (the method's arithmetic, not this kernel's): outside the contract. */
 int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale, const uint16_t* vbf,
               const float* v_scale, int B, int H, int Nq, int Nk, int D, float scale_log2, int causal, void* out,
               const int64_t out_str[3], int out_dtype, void* stream);
 
 /* Prefill over an INT8 KV cache with per-token scales (Strata #2092, description and
- * the "qsa_prompt_attn_parity (int8 KV)" table).
+ * the "qsa_prompt_attn_parity (int8 KV)" table); the loop is the one of qattn_fwd, with
+ * the same score domain.
  *   q: bf16 [Nq, H, D] view with strides q_str = {sn, sh}; query i sits at absolute
  *      position pos0 + i and sees keys 0 .. pos0 + i (0 <= pos0, pos0 + Nq <= Nk).
  *   k_cache, v_cache: int8 [H, Nk, D] contiguous; k_tok_scale, v_tok_scale: f32 [H, Nk]
  *      (one scale per head and token: value = code * scale).
- *   workspace: >= qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D) bytes, 256-byte aligned;
+ *   workspace: >= qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, kv_splits) bytes (kv_splits
+ *      resolved), 256-byte aligned;
  *      receives the per-channel e4m3 requantization of V (fl32(code * scale) quantized
  *      as in step 2 over all Nk tokens), held as the bf16 values of its codes, and the
  *      INT8 blocks of q (as in step 1, no smoothing).  Sections, each starting on a
@@ -130,8 +137,9 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
                    float scale_log2, int kv_splits, void* workspace, size_t workspace_bytes, void* out,
                    const int64_t out_str[2], int out_dtype, void* stream);
 
-/* Workspace size for qattn_fwd_i8kv with kv_splits key ranges (1 .. 64; resolve 0 with
- * qattn_fwd_i8kv_kv_splits first): H*D*4 (V scales) + H*Nq_pad*D (q codes) +
+/* Workspace size in bytes for qattn_fwd_i8kv(H, Nq, Nk, D, ..., kv_splits, ...) with
+ * kv_splits key ranges (1 .. 64; resolve 0 with qattn_fwd_i8kv_kv_splits first):
+ * H*D*4 (V scales) + H*Nq_pad*D (q codes) +
  * H*Nq_pad/64*4 (q scales) + H*D*Nk_pad*2 (bf16 values of the V codes), and for
  * kv_splits > 1 the partial results
  * kv_splits*H*Nq_pad*D*4 (O) + kv_splits*H*Nq_pad*8 (m, d'), each section rounded up to
@@ -158,17 +166,24 @@ int qattn_fwd_i8kv_kv_splits(int H, int Nq, int Nk, int pos0);
 int qattn_kv_append_i8(const void* x, const int64_t x_str[2], int Nnew, int H, int D, int8_t* cache,
                        float* tok_scale, int Nmax, int pos, void* stream);
 
-/* Self-test hook: codes[i] = E4M3(2^(u[i] - 80)) computed by the fused kernel's own
- * device functions (the FP8 P code the softmax produces for the grid argument u: the
- * hardware exponential of u, then the FP8 conversion with the exact 2^80 scale).
- * u: f32 [n], codes: u8 [n], device pointers.  Used to check the exponential against the
- * correctly rounded one over every argument the softmax can produce (u <= 88 + 2^-16).
- * Like the kernel, the conversion does not saturate: u > 88.86 (a power above 464, never
- * produced by the softmax) gives the NaN code 0x7F. */
-int qattn_p8_codes(const float* u, uint8_t* codes, int64_t n, void* stream);
-
 /* Static description of a status code. */
 const char* qattn_status_string(int status);
+
+/* ---- Self-test hook: not part of the attention interface ---------------------------
+ * codes[i] = the FP8 code of P' = 2^(u[i] - 80) as the fused kernel's softmax forms it
+ * for the exponent argument u[i] (the kernel's own device functions: the hardware
+ * exponential of u, then the FP8 conversion with the exact 2^80 scale), so that a test
+ * can compare it with the correctly rounded, saturating E4M3 of 2^(u - 80) over every
+ * argument the softmax can produce.
+ *   saturating = 0: the ordinary form, used while every row of a wave has |m| < 2^22
+ *     (m = running maximum of the log2-domain scores).  There u <= 88.375 + 2^-17.  The
+ *     conversion itself does not saturate: u >= 88.86 (a power of 464 or more) would give
+ *     the NaN code 0x7F.
+ *   saturating = 1: the large-score form (some row with |m| >= 2^22), where u is
+ *     unbounded above: the conversion input is clamped to 448 * 2^80, so every u above
+ *     88.81 (and an infinite power) gives 0x7E.
+ * u: f32 [n], codes: u8 [n], device pointers; n > 0. */
+int qattn_selftest_p8_codes(const float* u, uint8_t* codes, int64_t n, int saturating, void* stream);
 
 #ifdef __cplusplus
 }

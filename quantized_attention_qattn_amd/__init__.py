@@ -17,6 +17,7 @@ Layouts (N_pad = ceil(N / 64) * 64):
 """
 from __future__ import annotations
 
+import contextlib as _contextlib
 import ctypes as _ct
 import os
 
@@ -28,6 +29,10 @@ LIB_PATH = os.path.join(_HERE, "libqattn.so")
 QATTN_OK, QATTN_EINVAL, QATTN_EUNSUPPORTED, QATTN_EWORKSPACE, QATTN_EHIP = 0, -1, -2, -3, -4
 QATTN_OUT_BF16, QATTN_OUT_F32 = 0, 1
 BLOCK = 64
+# The matrix instruction of the fused loop's P.V product, and the bytes per V element of
+# the operand it reads (the bf16 values of the V codes, written by the preparation).
+PV_INSTRUCTION = "v_mfma_f32_32x32x16_bf16"
+V_OPERAND_BYTES = 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python quantized_attention_qattn_amd/_build.py`")
@@ -53,8 +58,8 @@ _lib.qattn_fwd_i8kv_kv_splits.argtypes = [_I, _I, _I, _I]
 _lib.qattn_fwd_i8kv_kv_splits.restype = _I
 _lib.qattn_kv_append_i8.argtypes = [_P, _I64x2, _I, _I, _I, _P, _P, _I, _I, _P]
 _lib.qattn_kv_append_i8.restype = _I
-_lib.qattn_p8_codes.argtypes = [_P, _P, _I64, _P]
-_lib.qattn_p8_codes.restype = _I
+_lib.qattn_selftest_p8_codes.argtypes = [_P, _P, _I64, _I, _P]
+_lib.qattn_selftest_p8_codes.restype = _I
 _lib.qattn_status_string.argtypes = [_I]
 _lib.qattn_status_string.restype = _ct.c_char_p
 
@@ -148,14 +153,16 @@ def qattn_prep(q, k, v, q8, q_scale, k8, k_scale, k_mean, v8t, v_scale, vbf=None
     _buf(k8, torch.int8, (B, H, npad(Nk), D), "k8")
     _buf(k_scale, torch.float32, (B, H, npad(Nk) // BLOCK), "k_scale")
     _buf(k_mean, torch.float32, (B, H, D), "k_mean")
-    _buf(v8t, torch.uint8, (B, H, D, npad(Nk)), "v8t")
+    if v8t is None and vbf is None:
+        raise ValueError("qattn_prep: v8t and vbf cannot both be None")
+    if v8t is not None:
+        _buf(v8t, torch.uint8, (B, H, D, npad(Nk)), "v8t")
     _buf(v_scale, torch.float32, (B, H, D), "v_scale")
     if vbf is not None:
         _buf(vbf, torch.bfloat16, (B, H, D, npad(Nk)), "vbf")
     _check(_lib.qattn_prep(_ptr(q), _I64x3(*q.stride()[:3]), _ptr(k), _I64x3(*k.stride()[:3]), _ptr(v),
                            _I64x3(*v.stride()[:3]), B, H, Nq, Nk, D, _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale),
-                           _ptr(k_mean), _ptr(v8t), _ptr(v_scale), None if vbf is None else _ptr(vbf),
-                           _stream(stream)), "qattn_prep")
+                           _ptr(k_mean), _ptr(v8t), _ptr(v_scale), _ptr(vbf), _stream(stream)), "qattn_prep")
 
 
 def qattn_fwd(q8, q_scale, k8, k_scale, vbf, v_scale, Nq: int, Nk: int, out, scale_log2: float = 0.0,
@@ -217,16 +224,27 @@ def qattn_kv_append_i8(x, cache, tok_scale, pos: int, stream=None) -> None:
                                    int(pos), _stream(stream)), "qattn_kv_append_i8")
 
 
-def qattn_p8_codes(u, codes, stream=None) -> None:
+def qattn_selftest_p8_codes(u, codes, saturating: bool = False, stream=None) -> None:
+    """Self-test hook (not part of the attention interface): the FP8 code of P' the
+    fused kernel's softmax forms for each exponent argument u."""
     _need(u, torch.float32, "u")
     _buf(u, torch.float32, (u.numel(),), "u")
     _buf(codes, torch.uint8, (u.numel(),), "codes")
-    _check(_lib.qattn_p8_codes(_ptr(u), _ptr(codes), u.numel(), _stream(stream)), "qattn_p8_codes")
+    _check(_lib.qattn_selftest_p8_codes(_ptr(u), _ptr(codes), u.numel(), 1 if saturating else 0, _stream(stream)),
+           "qattn_selftest_p8_codes")
 
 
 # ----------------------------------------------------------------------------------
 # allocation helpers (torch owns the memory; the library allocates nothing)
 # ----------------------------------------------------------------------------------
+def _alloc_on(stream):
+    """Allocations for a call on `stream` are made on that stream, so that the caching
+    allocator does not hand their memory to other work before the call's kernels ran."""
+    if stream is None or not isinstance(stream, torch.cuda.Stream):
+        return _contextlib.nullcontext()
+    return torch.cuda.stream(stream)
+
+
 def alloc_qk(B: int, H: int, Nq: int, Nk: int, D: int, device="cuda"):
     kw = dict(device=device)
     return dict(
@@ -238,32 +256,55 @@ def alloc_qk(B: int, H: int, Nq: int, Nk: int, D: int, device="cuda"):
     )
 
 
-def alloc_v(B: int, H: int, Nk: int, D: int, device="cuda"):
-    return dict(v8t=torch.empty((B, H, D, npad(Nk)), dtype=torch.uint8, device=device),
-                v_scale=torch.empty((B, H, D), dtype=torch.float32, device=device),
-                vbf=torch.empty((B, H, D, npad(Nk)), dtype=torch.bfloat16, device=device))
+def alloc_v(B: int, H: int, Nk: int, D: int, device="cuda", codes: bool = True):
+    """v_scale and the loop's V operand vbf, and with codes=True the e4m3 codes v8t."""
+    t = dict(v_scale=torch.empty((B, H, D), dtype=torch.float32, device=device),
+             vbf=torch.empty((B, H, D, npad(Nk)), dtype=torch.bfloat16, device=device))
+    if codes:
+        t["v8t"] = torch.empty((B, H, D, npad(Nk)), dtype=torch.uint8, device=device)
+    return t
+
+
+def alloc_prep(B: int, H: int, Nq: int, Nk: int, D: int, device="cuda", codes: bool = False):
+    """Every buffer qattn_prep writes for a later qattn_fwd (the V codes only with codes=True)."""
+    return {**alloc_qk(B, H, Nq, Nk, D, device), **alloc_v(B, H, Nk, D, device, codes)}
+
+
+def prep_into(q, k, v, t: dict, stream=None) -> None:
+    """qattn_prep into the buffers of alloc_prep."""
+    qattn_prep(q, k, v, t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["k_mean"], t.get("v8t"), t["v_scale"],
+               t["vbf"], stream)
+
+
+def fwd_from(t: dict, Nq: int, Nk: int, out, scale_log2: float = 0.0, causal: bool = False, stream=None) -> None:
+    """qattn_fwd on the buffers of alloc_prep."""
+    qattn_fwd(t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["vbf"], t["v_scale"], Nq, Nk, out, scale_log2, causal,
+              stream)
 
 
 def quant_qk(q, k, stream=None):
     B, Nq, H, D = q.shape
-    t = alloc_qk(B, H, Nq, k.shape[1], D, q.device)
+    with _alloc_on(stream):
+        t = alloc_qk(B, H, Nq, k.shape[1], D, q.device)
     qattn_quant_qk(q, k, t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["k_mean"], stream)
     return t
 
 
 def quant_v(v, stream=None):
     B, Nk, H, D = v.shape
-    t = alloc_v(B, H, Nk, D, v.device)
+    with _alloc_on(stream):
+        t = alloc_v(B, H, Nk, D, v.device)
     qattn_quant_v(v, t["v8t"], t["v_scale"], t["vbf"], stream)
     return t
 
 
-def prep(q, k, v, stream=None):
-    """Steps 1-2 through the fused preparation; returns the intermediates of quant_qk and quant_v."""
+def prep(q, k, v, stream=None, codes: bool = True):
+    """Steps 1-2 through the fused preparation; returns the intermediates of quant_qk and
+    quant_v (the V codes v8t only with codes=True)."""
     B, Nq, H, D = q.shape
-    t = {**alloc_qk(B, H, Nq, k.shape[1], D, q.device), **alloc_v(B, H, k.shape[1], D, q.device)}
-    qattn_prep(q, k, v, t["q8"], t["q_scale"], t["k8"], t["k_scale"], t["k_mean"], t["v8t"], t["v_scale"], t["vbf"],
-               stream)
+    with _alloc_on(stream):
+        t = alloc_prep(B, H, Nq, k.shape[1], D, q.device, codes)
+    prep_into(q, k, v, t, stream)
     return t
 
 
@@ -272,9 +313,9 @@ def attention(q, k, v, causal: bool = False, scale_log2: float = 0.0, out_dtype=
     returns (out [B, Nq, H, D], intermediates)."""
     B, Nq, H, D = q.shape
     qk = prep(q, k, v, stream)
-    out = torch.empty((B, Nq, H, D), dtype=out_dtype, device=q.device)
-    qattn_fwd(qk["q8"], qk["q_scale"], qk["k8"], qk["k_scale"], qk["vbf"], qk["v_scale"], Nq, k.shape[1], out,
-              scale_log2, causal, stream)
+    with _alloc_on(stream):
+        out = torch.empty((B, Nq, H, D), dtype=out_dtype, device=q.device)
+    fwd_from(qk, Nq, k.shape[1], out, scale_log2, causal, stream)
     return out, qk
 
 
@@ -284,11 +325,13 @@ def attention_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, sca
     Nq, H, D = q.shape
     Nk = k_cache.shape[1]
     S = kv_splits if kv_splits > 0 else qattn_fwd_i8kv_kv_splits(H, Nq, Nk, pos0)
-    ws = torch.empty(qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, S), dtype=torch.uint8, device=q.device)
-    out = torch.empty((Nq, H, D), dtype=out_dtype, device=q.device)
+    with _alloc_on(stream):
+        ws = torch.empty(qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, S), dtype=torch.uint8, device=q.device)
+        out = torch.empty((Nq, H, D), dtype=out_dtype, device=q.device)
     qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0, ws, out, scale_log2, stream, kv_splits=S)
     return out, ws
 
 
-__all__ = [n for n in dir() if n.startswith("qattn_")] + ["attention", "attention_i8kv", "prep", "quant_qk", "quant_v",
-                                                           "alloc_qk", "alloc_v", "QattnError", "LIB_PATH"]
+__all__ = [n for n in dir() if n.startswith("qattn_")] + ["attention", "attention_i8kv", "prep", "prep_into", "fwd_from",
+                                                           "quant_qk", "quant_v", "alloc_qk", "alloc_v", "alloc_prep",
+                                                           "QattnError", "LIB_PATH", "PV_INSTRUCTION", "V_OPERAND_BYTES"]

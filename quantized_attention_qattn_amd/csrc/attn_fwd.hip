@@ -73,8 +73,13 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | n; }
 // equals the code of the correctly rounded power (checked over every fp32 u through
 // qattn_p8_codes).
 constexpr float kPScale = 0x1p80f;     // P'' / P'
-[[maybe_unused]] constexpr float kPScaleInv = 0x1p-80f;
+constexpr float kPScaleInv = 0x1p-80f;
 __device__ __forceinline__ float p_from_u(float u) { return __builtin_amdgcn_exp2f(u); }
+// The large-score form (see softmax_tile): the FP8 conversion does not saturate (a value
+// of 464 or more gives the NaN code), so its input is clamped to 448 * 2^80, whose code
+// is the saturated one (0x7E).
+constexpr float kPSat = 448.0f * 0x1p80f;
+__device__ __forceinline__ float p_code_input_saturating(float p) { return __builtin_fminf(p, kPSat); }
 typedef short v2s_t __attribute__((ext_vector_type(2)));
 
 // e4m3 codes of P' = P'' / 2^80 for four values (bytes 0..3).  Both halves of the word
@@ -244,7 +249,7 @@ __device__ __forceinline__ int select_visible_or_zero(int x, int lim) {
 // factor alpha of the old terms).
 template <bool MASKED, bool PER_TOKEN>
 __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, const float* cp, float c_tile,
-                                            int key0, int vis_last, float& m, float& tsum) {
+                                            int key0, int vis_last, float& m, float& tsum, float (&p)[32]) {
   float cvec[32];
   if (PER_TOKEN) {
 #pragma unroll
@@ -267,12 +272,18 @@ __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, cons
     accv[i] = S0[i];
     accv[16 + i] = S1[i];
   }
+  // exact fp32 dot products.  With per-block scales they are formed first, while the tile
+  // max (on the integers) is pending; with per-token scales the max needs them anyway.
+  float accf[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) accf[i] = PER_TOKEN ? 0.0f : acc_f32(accv[i]);
+  auto af = [&](int i) { return PER_TOKEN ? acc_f32(accv[i]) : accf[i]; };
   float Mt;
   if (PER_TOKEN) {
     Mt = -INFINITY;
     static_for<32>([&](auto i_c) {
       constexpr int i = decltype(i_c)::value;
-      float sv = acc_f32(accv[i]) * cvec[i];
+      float sv = af(i) * cvec[i];
       if (MASKED) sv = __builtin_bit_cast(float, select_visible<i>(__builtin_bit_cast(int, sv), lim, ninf));
       Mt = fmaxf(Mt, sv);
     });
@@ -306,10 +317,10 @@ __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, cons
   // i.e. 2^80 times an fp32 sum of P')
   float ds[4];
   v8i pf;
-  float p[32], u0[8];
+  float u0[8];
   static_for<32>([&](auto i_c) {
     constexpr int i = decltype(i_c)::value;
-    float u = __builtin_fmaf(acc_f32(accv[i]), PER_TOKEN ? cvec[i] : c_tile, bconst);
+    float u = __builtin_fmaf(af(i), PER_TOKEN ? cvec[i] : c_tile, bconst);
     if (MASKED) u = __builtin_bit_cast(float, select_visible<i>(__builtin_bit_cast(int, u), lim, ninf));
     p[i] = p_from_u(u);
     if (i % 4 == 0) u0[i / 4] = u;
@@ -318,6 +329,30 @@ __device__ __forceinline__ v8i softmax_tile(const v16i& S0, const v16i& S1, cons
 #pragma unroll
   for (int w = 0; w < 8; ++w) pf[w] = pack_fp8x4(u0[w], p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3]);
   tsum = (ds[0] + ds[1]) + (ds[2] + ds[3]);
+  return pf;
+}
+
+// The large-score form of a tile's results from its powers p = 2^u = 2^80 P'.
+// u = fl32(acc c + fl32(88 - m_s)) exceeds 88 by at most (ulp(m_s) + ulp(88 - m_s)) / 2
+// + ulp(u) / 2, i.e. by at most 0.375 + 2^-17 while |m_s| < 2^22: then P' <= 2^8.375 < 448
+// and no code saturates.  Beyond, u may pass 88.81, where P' exceeds 448 and its code
+// saturates; for |m_s| < 2^28 (the contract's score domain) u stays below 112 and 2^u is
+// finite.  From the first tile where some row of a wave has |m_s| >= 2^22 the wave stays
+// in this form: the codes are formed again from min(2^u, 448 * 2^80) and the tile's sum
+// from P' = 2^-80 2^u, so d' is kept unscaled (a sum of up to 2^28 values of 2^112 would
+// overflow).  It replaces the ordinary form's results, which are formed first.
+__device__ __forceinline__ v8i large_score_form(const float (&p)[32], float& tsum) {
+  float ds[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ds[j] = p[j] * kPScaleInv;
+#pragma unroll
+  for (int i = 4; i < 32; ++i) ds[i & 3] = ds[i & 3] + p[i] * kPScaleInv;
+  tsum = (ds[0] + ds[1]) + (ds[2] + ds[3]);
+  v8i pf;
+#pragma unroll
+  for (int w = 0; w < 8; ++w)
+    pf[w] = pack_fp8x4(p[4 * w], p_code_input_saturating(p[4 * w]), p_code_input_saturating(p[4 * w + 1]),
+                       p_code_input_saturating(p[4 * w + 2]), p_code_input_saturating(p[4 * w + 3]));
   return pf;
 }
 
@@ -480,6 +515,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   };
   float m = -INFINITY;  // running max (log2 domain)
   float dsum = 0.0f;    // this lane's share of d'' = 2^80 d' (its 32 keys of every tile)
+  bool big = false;     // wave-uniform: the large-score form (see softmax_tile)
+  float dscale = kPScaleInv;  // d' / (sum of dsum): 2^-80, or 1 in the large-score form
   v16f O[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
@@ -615,17 +652,32 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
       float tsum;
       v8i pf;
       const float m_old = m;
+      float p[32];
       if (masked) {
         const int vis_last = (int)min(CAUSAL ? (int64_t)qrow + a.pos_off : (int64_t)a.Nk - 1, (int64_t)a.Nk - 1);
-        pf = softmax_tile<true, PER_TOKEN>(S0, S1, cp, c_tile, key0, vis_last, m, tsum);
+        pf = softmax_tile<true, PER_TOKEN>(S0, S1, cp, c_tile, key0, vis_last, m, tsum, p);
       } else {
-        pf = softmax_tile<false, PER_TOKEN>(S0, S1, cp, c_tile, key0, 0, m, tsum);
+        pf = softmax_tile<false, PER_TOKEN>(S0, S1, cp, c_tile, key0, 0, m, tsum, p);
       }
       // alpha = 2^(m_old - m) rescales the old terms of d'' and O; it is exactly 1 for a
       // row whose maximum stayed (d'' * 1 = d''), so the exponential, the product and the
-      // rescale run only when some row of the wave has a new maximum (then m is finite)
-      if (__ballot(m != m_old) != 0) {
+      // rescale run only when some row of the wave has a new maximum (then m is finite).
+      // The large-score form (large_score_form) is entered on such a tile too: |m_s|
+      // grows only with m.
+      const bool moved = __ballot(m != m_old) != 0;
+      if (moved && !big) {
+        const float am = __builtin_fabsf(m);
+        big = __ballot(am >= 0x1p22f && am < INFINITY) != 0;
+      }
+      if (__builtin_expect(big, 0)) pf = large_score_form(p, tsum);
+      if (moved) {
         const float alpha = m == m_old ? 1.0f : __builtin_amdgcn_exp2f(m_old - m);
+        // entering the large-score form: the sum so far holds P'' = 2^80 P' and is brought
+        // to P' (exact for every partial sum above 2^-46; smaller ones lie far below d')
+        if (big && dscale != 1.0f) {
+          dsum *= kPScaleInv;
+          dscale = 1.0f;
+        }
         dsum = dsum * alpha + tsum;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -681,7 +733,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
   }
 
   // ---- epilogue: out = O * s_v / d' ----
-  const float dt = sum_with_partner(dsum) * kPScaleInv;  // d' = d'' / 2^80, exact
+  const float dt = sum_with_partner(dsum) * dscale;  // d' = d'' / 2^80 (exact), or d' itself
   if (a.kv_splits > 1) {  // partial result of this key range, combined by attn_combine_kernel
     if (qrow < a.Nq) {
       const int64_t prow = ((int64_t)split * (a.B * a.H) + bh) * a.nq_pad + qrow;
@@ -723,11 +775,17 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(FwdArgs a) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-__global__ void p8_codes_kernel(const float* u, uint8_t* codes, int64_t n) {
+// The FP8 code of P' that the softmax produces for exponent argument u: in the ordinary
+// form (saturating = 0) and in the large-score form (saturating = 1).
+__global__ void p8_codes_kernel(const float* u, uint8_t* codes, int64_t n, int saturating) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    codes[i] = (uint8_t)(__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
-                             v2s_t{0, 0}, p_from_u(u[i]), 0.0f, kPScale, false)) & 0xff);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    float p = p_from_u(u[i]);
+    if (saturating) p = p_code_input_saturating(p);
+    codes[i] = (uint8_t)(__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s_t{0, 0}, p, 0.0f,
+                                                                                            kPScale, false)) &
+                         0xff);
+  }
 }
 
 // Split-KV combine: one thread per (b, h, query row, 4 channels).  Per row, in split
@@ -805,11 +863,11 @@ hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st) {
   return D == 128 ? launch_d<128>(a, st) : launch_d<64>(a, st);
 }
 
-hipError_t launch_p8_codes(const float* u, uint8_t* codes, int64_t n, hipStream_t st) {
+hipError_t launch_p8_codes(const float* u, uint8_t* codes, int64_t n, int saturating, hipStream_t st) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  p8_codes_kernel<<<(int)blocks, 256, 0, st>>>(u, codes, n);
+  p8_codes_kernel<<<(int)blocks, 256, 0, st>>>(u, codes, n, saturating);
   return hipGetLastError();
 }
 

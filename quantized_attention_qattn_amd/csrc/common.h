@@ -117,6 +117,6 @@ struct FwdArgs {
 hipError_t launch_kv_append_i8(const void* x, int64_t sn, int64_t sh, int Nnew, int H, int D, int8_t* cache,
                                float* tok_scale, int Nmax, int pos, hipStream_t st);
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st);  // both kernels when split
-hipError_t launch_p8_codes(const float* u, uint8_t* codes, int64_t n, hipStream_t st);
+hipError_t launch_p8_codes(const float* u, uint8_t* codes, int64_t n, int saturating, hipStream_t st);
 
 }  // namespace qattn

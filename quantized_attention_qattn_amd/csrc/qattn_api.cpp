@@ -101,11 +101,12 @@ int qattn_quant_v(const void* v, const int64_t v_str[3], int B, int H, int Nk, i
 int qattn_prep(const void* q, const int64_t q_str[3], const void* k, const int64_t k_str[3], const void* v,
                const int64_t v_str[3], int B, int H, int Nq, int Nk, int D, int8_t* q8, float* q_scale, int8_t* k8,
                float* k_scale, float* k_mean, uint8_t* v8t, float* v_scale, uint16_t* vbf, void* stream) {
-  if (!q8 || !q_scale || !k8 || !k_scale || !k_mean || !v8t || !v_scale) return QATTN_EINVAL;
+  if (!q8 || !q_scale || !k8 || !k_scale || !k_mean || !v_scale || (!v8t && !vbf)) return QATTN_EINVAL;
   if (!bf16_view_ok(q, q_str, 3) || !bf16_view_ok(k, k_str, 3) || !bf16_view_ok(v, v_str, 3)) return QATTN_EINVAL;
   if (!sizes_ok(B, H, Nq) || !sizes_ok(B, H, Nk)) return QATTN_EINVAL;
   if (D != 64 && D != 128) return QATTN_EUNSUPPORTED;
-  if (!aligned(q8, 256) || !aligned(k8, 256) || !aligned(v8t, 256) || (vbf && !aligned(vbf, 256))) return QATTN_EINVAL;
+  if (!aligned(q8, 256) || !aligned(k8, 256) || (v8t && !aligned(v8t, 256)) || (vbf && !aligned(vbf, 256)))
+    return QATTN_EINVAL;
   if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(k_mean, 4) || !aligned(v_scale, 4)) return QATTN_EINVAL;
   PrepArgs p{};
   p.q = BshdView{q, q_str[0], q_str[1], q_str[2]};
@@ -315,10 +316,10 @@ int qattn_kv_append_i8(const void* x, const int64_t x_str[2], int Nnew, int H, i
                                        (hipStream_t)stream));
 }
 
-int qattn_p8_codes(const float* u, uint8_t* codes, int64_t n, void* stream) {
-  if (!u || !codes || n <= 0) return QATTN_EINVAL;
+int qattn_selftest_p8_codes(const float* u, uint8_t* codes, int64_t n, int saturating, void* stream) {
+  if (!u || !codes || n <= 0 || (saturating != 0 && saturating != 1)) return QATTN_EINVAL;
   if (!aligned(u, 4)) return QATTN_EINVAL;
-  return status_of(launch_p8_codes(u, codes, n, (hipStream_t)stream));
+  return status_of(launch_p8_codes(u, codes, n, saturating, (hipStream_t)stream));
 }
 
 }  // extern "C"

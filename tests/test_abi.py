@@ -36,7 +36,7 @@ def lib():
     L.qattn_fwd_i8kv_workspace_bytes.restype = ct.c_size_t
     L.qattn_fwd_i8kv_kv_splits.argtypes = [I, I, I, I]
     L.qattn_fwd_i8kv_kv_splits.restype = I
-    L.qattn_p8_codes.argtypes = [P, P, ct.c_int64, P]
+    L.qattn_selftest_p8_codes.argtypes = [P, P, ct.c_int64, ct.c_int, P]
     L.qattn_kv_append_i8.argtypes = [P, I64x2, I, I, I, P, P, I, I, P]
     L.qattn_status_string.argtypes = [I]
     L.qattn_status_string.restype = ct.c_char_p
@@ -52,7 +52,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["qattn_quant_qk", "qattn_quant_v", "qattn_prep", "qattn_fwd", "qattn_fwd_i8kv", "qattn_fwd_i8kv_workspace_bytes",
-              "qattn_fwd_i8kv_kv_splits", "qattn_kv_append_i8", "qattn_status_string", "qattn_p8_codes"]:
+              "qattn_fwd_i8kv_kv_splits", "qattn_kv_append_i8", "qattn_status_string", "qattn_selftest_p8_codes"]:
         assert n in names
 
 
@@ -136,7 +136,8 @@ def test_prep_validation(lib):
                               a["v_scale"], a["vbf"], None)
 
     assert call(v=None) == EINVAL
-    assert call(v8t=None) == EINVAL
+    assert call(v8t=None) == EINVAL  # neither the codes nor their bf16 values requested
+    assert call(v8t=None, vbf=A + 16) == EINVAL  # vbf alone, but not 256-byte aligned
     assert call(k_mean=None) == EINVAL
     assert call(D=96) == EUNSUP
     assert call(Nk=0) == EINVAL
@@ -206,8 +207,9 @@ def test_kv_append_validation(lib):
 
 
 def test_p8_codes_validation(lib):
-    assert lib.qattn_p8_codes(None, A, 10, None) == EINVAL
-    assert lib.qattn_p8_codes(A, A, 0, None) == EINVAL
+    assert lib.qattn_selftest_p8_codes(None, A, 10, 0, None) == EINVAL
+    assert lib.qattn_selftest_p8_codes(A, A, 0, 0, None) == EINVAL
+    assert lib.qattn_selftest_p8_codes(A, A, 10, 2, None) == EINVAL
 
 
 def test_product_path_does_not_use_the_oracle():

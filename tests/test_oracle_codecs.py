@@ -137,7 +137,41 @@ def test_p8_code_grid_properties(orc):
     assert at(80.0 - 9.0) == 0x01  # x = -9 -> 2^-9
     assert at(80.0 - 10.0) == 0x00  # 2^-10: half the smallest subnormal, ties to even (0)
     assert at(80.0 - 11.0) == 0x00  # below half the smallest subnormal
-    assert codes.max() <= 0x7E  # the oracle saturates; the softmax never exceeds u = 88 + 2^-16
+    assert codes.max() <= 0x7E  # the oracle's encoder saturates at 448
+    assert (codes[u > np.float32(88.81)] == 0x7E).all()  # P' = 2^(u - 80) > 448: saturated
+
+
+def _exponent_arguments(rng, n, m_mag):
+    """u = fl32(acc * c + fl32(88 - m_s)) for rows whose running max m_s = fl32(acc_max * c)
+    has magnitude about m_mag (the softmax's exponent argument, computed exactly in
+    fractions-free double arithmetic: acc * c is exact in double, the sum is rounded once
+    to double and then to fp32, which cannot cross an fp32 rounding boundary here)."""
+    acc_max = rng.integers(1 << 20, 1 << 21, n)
+    acc = acc_max - rng.integers(0, 4, n)  # keys at or just below the row maximum
+    sign = rng.choice([-1, 1], n)
+    c = (m_mag / acc_max * rng.uniform(0.5, 2.0, n)).astype(np.float32)
+    acc_max, acc = acc_max * sign, acc * sign
+    m_s = (acc_max.astype(np.float64) * c.astype(np.float64)).astype(np.float32)
+    m_s = np.maximum(m_s, (acc.astype(np.float64) * c.astype(np.float64)).astype(np.float32))
+    b = (np.float32(88.0) - m_s).astype(np.float32)
+    u = (acc.astype(np.float64) * c.astype(np.float64) + b.astype(np.float64)).astype(np.float32)
+    return u, m_s
+
+
+def test_exponent_argument_bound():
+    """The bound the fused kernel's two softmax forms rest on: while |m_s| < 2^22 the
+    exponent argument u exceeds 88 by at most (ulp(m_s) + ulp(88 - m_s)) / 2 + ulp(u) / 2
+    <= 0.375 + 2^-17, so P' = 2^(u - 80) < 448 and no P code saturates; for larger |m_s|
+    the argument passes 88.81 (saturated codes), which is why the kernel switches to its
+    saturating form there."""
+    rng = np.random.default_rng(11)
+    for mag in (1.0, 2.0 ** 10, 2.0 ** 20, 2.0 ** 21.9):
+        u, m_s = _exponent_arguments(rng, 200_000, mag)
+        keep = np.abs(m_s) < 2.0 ** 22
+        assert keep.sum() > 50_000
+        assert u[keep].max() <= 88.375 + 2.0 ** -17, mag
+    u, m_s = _exponent_arguments(rng, 200_000, 2.0 ** 24)
+    assert (u > 88.81).any()  # reachable: the saturating form is needed
 
 
 def test_bf16_rounding(orc):
