@@ -29,7 +29,7 @@ TILE = 64
 _lock = threading.Lock()
 _lib = None
 
-_CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+_CFLAGS = ["-O3", "-march=x86-64-v3", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 
 def build(force: bool = True) -> str:

@@ -6,7 +6,7 @@
  * constant generator with the HIP library; the two are written independently from
  * the same numeric contract.
  *
- * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
+ * Build: gcc -O3 -march=x86-64-v3 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
  * (no FMA contraction, no reassociation: every fp32 rounding below is explicit).
  *
  * Method (from the pages):
@@ -358,9 +358,16 @@ void orc_attn_rows_part(const int8_t* q8, const float* qs, const int8_t* k8, con
   float* Sv = (float*)malloc(sizeof(float) * ORC_TILE);
   int32_t* acc = (int32_t*)malloc(sizeof(int32_t) * ORC_TILE);
   uint8_t* P8 = (uint8_t*)malloc(ORC_TILE);
-  float* vdec = (float*)malloc(sizeof(float) * ORC_TILE * D); /* [key][c] of the tile */
   float dec_tab[256];
   for (int c = 0; c < 256; ++c) dec_tab[c] = (float)orc_e4m3_decode((uint8_t)c);
+  /* the decoded V values of the keys these tiles cover, token-major [key][c] (decoded once
+   * per call rather than once per row: a table of exact values, no arithmetic) */
+  int64_t j_lo = (int64_t)t_lo * ORC_TILE, j_hi = (int64_t)t_hi * ORC_TILE;
+  if (j_hi > Nk) j_hi = Nk;
+  if (j_lo > j_hi) j_lo = j_hi;
+  float* vdec = (float*)malloc(sizeof(float) * (size_t)(j_hi - j_lo + 1) * D);
+  for (int64_t j = j_lo; j < j_hi; ++j)
+    for (int c = 0; c < D; ++c) vdec[(j - j_lo) * D + c] = dec_tab[v8t[(int64_t)c * ldv + j]];
 
   for (int i = i0; i < i1; ++i) {
     const int8_t* qrow = q8 + (int64_t)i * D;
@@ -408,15 +415,11 @@ void orc_attn_rows_part(const int8_t* q8, const float* qs, const int8_t* k8, con
       for (int jj = 0; jj < ORC_TILE; ++jj) P8[jj] = orc_e4m3_encode(Pp[jj]);
       /* PV: products of two E4M3 values are exact in fp32 */
       for (int jj = 0; jj < ORC_TILE; ++jj) {
-        int j = j0 + jj;
-        if (Sv[jj] == -INFINITY) continue;
-        for (int c = 0; c < D; ++c) vdec[jj * D + c] = dec_tab[v8t[(int64_t)c * ldv + j]];
-      }
-      for (int jj = 0; jj < ORC_TILE; ++jj) {
         if (Sv[jj] == -INFINITY) continue;
         float p = dec_tab[P8[jj]];
         if (p == 0.0f) continue; /* adds exact zeros */
-        for (int c = 0; c < D; ++c) O[c] = O[c] + p * vdec[jj * D + c];
+        const float* vrow = vdec + ((int64_t)(j0 + jj) - j_lo) * D;
+        for (int c = 0; c < D; ++c) O[c] = O[c] + p * vrow[c];
       }
       m = mnew;
     }
