@@ -41,7 +41,8 @@ typedef enum {
   QATTN_EINVAL = -1,        /* null pointer, bad size, misalignment, bad stride, pos0 out of range */
   QATTN_EUNSUPPORTED = -2,  /* D not in {64, 128} */
   QATTN_EWORKSPACE = -3,    /* workspace smaller than qattn_fwd_i8kv_workspace_bytes() */
-  QATTN_EHIP = -4           /* a kernel launch failed */
+  QATTN_EHIP = -4,          /* a kernel launch failed */
+  QATTN_ESCRATCH = -5       /* qattn_fwd_i8kv_noalloc: the call needs more than QATTN_NOALLOC_SCRATCH_BYTES */
 } qattn_status;
 
 typedef enum { QATTN_OUT_BF16 = 0, QATTN_OUT_F32 = 1 } qattn_out_dtype;
@@ -136,6 +137,23 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
                    const int8_t* v_cache, const float* v_tok_scale, int H, int Nq, int Nk, int D, int pos0,
                    float scale_log2, int kv_splits, void* workspace, size_t workspace_bytes, void* out,
                    const int64_t out_str[2], int out_dtype, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, hosts that forbid hipMalloc): qattn_fwd_i8kv with the same arguments
+ * minus the workspace, which lives instead in a device array of the library holding
+ * QATTN_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on (kept until the process ends).
+ * The call allocates nothing.  Returns QATTN_ESCRATCH, before any launch, when the call
+ * would need a larger workspace than that (qattn_fwd_i8kv_workspace_bytes with the
+ * resolved kv_splits), e.g. 32 heads of D = 128 and 512 queries over 24K or more cached tokens;
+ * every other argument is checked as by qattn_fwd_i8kv.  All calls on one GPU share its
+ * array: calls that overlap on one GPU (other streams, other threads) race and give
+ * undefined results.  A call leaves its intermediates in the array; nothing needs to be
+ * cleared between calls. */
+#define QATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int qattn_fwd_i8kv_noalloc(const void* q, const int64_t q_str[2], const int8_t* k_cache, const float* k_tok_scale,
+                           const int8_t* v_cache, const float* v_tok_scale, int H, int Nq, int Nk, int D, int pos0,
+                           float scale_log2, int kv_splits, void* out, const int64_t out_str[2], int out_dtype,
+                           void* stream);
 
 /* Workspace size in bytes for qattn_fwd_i8kv(H, Nq, Nk, D, ..., kv_splits, ...) with
  * kv_splits key ranges (1 .. 64; resolve 0 with qattn_fwd_i8kv_kv_splits first):

@@ -26,7 +26,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqattn.so")
 
-QATTN_OK, QATTN_EINVAL, QATTN_EUNSUPPORTED, QATTN_EWORKSPACE, QATTN_EHIP = 0, -1, -2, -3, -4
+QATTN_OK, QATTN_EINVAL, QATTN_EUNSUPPORTED, QATTN_EWORKSPACE, QATTN_EHIP, QATTN_ESCRATCH = 0, -1, -2, -3, -4, -5
+QATTN_NOALLOC_SCRATCH_BYTES = 256 << 20  # the static workspace of qattn_fwd_i8kv_noalloc, per GPU
 QATTN_OUT_BF16, QATTN_OUT_F32 = 0, 1
 BLOCK = 64
 # The matrix instruction of the fused loop's P.V product, and the bytes per V element of
@@ -52,6 +53,8 @@ _lib.qattn_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _
 _lib.qattn_fwd.restype = _I
 _lib.qattn_fwd_i8kv.argtypes = [_P, _I64x2, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P, _I64x2, _I, _P]
 _lib.qattn_fwd_i8kv.restype = _I
+_lib.qattn_fwd_i8kv_noalloc.argtypes = [_P, _I64x2, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _I64x2, _I, _P]
+_lib.qattn_fwd_i8kv_noalloc.restype = _I
 _lib.qattn_fwd_i8kv_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.qattn_fwd_i8kv_workspace_bytes.restype = _SZ
 _lib.qattn_fwd_i8kv_kv_splits.argtypes = [_I, _I, _I, _I]
@@ -209,6 +212,25 @@ def qattn_fwd_i8kv(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, wor
                                _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _ptr(out), _I64x2(*out.stride()[:2]), od,
                                _stream(stream)), "qattn_fwd_i8kv")
+
+
+def qattn_fwd_i8kv_noalloc(q, k_cache, k_tok_scale, v_cache, v_tok_scale, pos0: int, out, scale_log2: float = 0.0,
+                           stream=None, kv_splits: int = 0) -> None:
+    """qattn_fwd_i8kv with the library's static per-GPU workspace (allocates nothing)."""
+    _need(q, torch.bfloat16, "q")
+    Nq, H, D = q.shape
+    Nk = k_cache.shape[1]
+    _buf(k_cache, torch.int8, (H, Nk, D), "k_cache")
+    _buf(k_tok_scale, torch.float32, (H, Nk), "k_tok_scale")
+    _buf(v_cache, torch.int8, (H, Nk, D), "v_cache")
+    _buf(v_tok_scale, torch.float32, (H, Nk), "v_tok_scale")
+    if not out.is_cuda or tuple(out.shape) != (Nq, H, D) or out.stride(2) != 1:
+        raise ValueError(f"out: expected a CUDA [Nq, H, D] = {(Nq, H, D)} view with unit channel stride")
+    od = QATTN_OUT_BF16 if out.dtype == torch.bfloat16 else QATTN_OUT_F32 if out.dtype == torch.float32 else -1
+    _check(_lib.qattn_fwd_i8kv_noalloc(_ptr(q), _I64x2(*q.stride()[:2]), _ptr(k_cache), _ptr(k_tok_scale),
+                                       _ptr(v_cache), _ptr(v_tok_scale), H, Nq, Nk, D, int(pos0), float(scale_log2),
+                                       int(kv_splits), _ptr(out), _I64x2(*out.stride()[:2]), od, _stream(stream)),
+           "qattn_fwd_i8kv_noalloc")
 
 
 def qattn_kv_append_i8(x, cache, tok_scale, pos: int, stream=None) -> None:

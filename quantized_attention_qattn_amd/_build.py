@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqattn.so")
-SOURCES = ["quant.hip", "attn_fwd.hip", "qattn_api.cpp"]
+SOURCES = ["quant.hip", "attn_fwd.hip", "qattn_api.cpp", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

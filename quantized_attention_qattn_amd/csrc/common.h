@@ -119,4 +119,17 @@ hipError_t launch_kv_append_i8(const void* x, int64_t sn, int64_t sh, int Nnew, 
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st);  // both kernels when split
 hipError_t launch_p8_codes(const float* u, uint8_t* codes, int64_t n, int saturating, hipStream_t st);
 
+// The prefill call (qattn_fwd_i8kv) in two parts: validation of everything but the
+// workspace (resolves *kv_splits, returns the workspace size in *need; no HIP call), and
+// the launches into a workspace of at least that size, 256-byte aligned.  Both return a
+// qattn_status.
+int i8kv_check(const void* q, const int64_t q_str[2], const int8_t* k_cache, const float* k_tok_scale,
+               const int8_t* v_cache, const float* v_tok_scale, int H, int Nq, int Nk, int D, int pos0,
+               float scale_log2, int* kv_splits, const void* out, const int64_t out_str[2], int out_dtype,
+               size_t* need);
+int i8kv_launch(const void* q, const int64_t q_str[2], const int8_t* k_cache, const float* k_tok_scale,
+                const int8_t* v_cache, const float* v_tok_scale, int H, int Nq, int Nk, int D, int pos0,
+                float scale_log2, int kv_splits, void* workspace, void* out, const int64_t out_str[2],
+                int out_dtype, void* stream);
+
 }  // namespace qattn

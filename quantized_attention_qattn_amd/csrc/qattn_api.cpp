@@ -49,6 +49,22 @@ inline float resolve_lambda(float scale_log2, int D) {
   return inv * log2e;
 }
 
+inline bool out_ok(const void* out, const int64_t* str, int n, int out_dtype) {
+  if (!out || !str) return false;
+  if (out_dtype != QATTN_OUT_BF16 && out_dtype != QATTN_OUT_F32) return false;
+  const int esz = out_dtype == QATTN_OUT_BF16 ? 2 : 4;
+  if (!aligned(out, 4 * esz)) return false;
+  for (int i = 0; i < n; ++i)
+    if (str[i] < 0 || (str[i] & 3) != 0) return false;
+  return true;
+}
+
+// Key tiles a causal prefill reads: every query sees keys 0 .. pos0 + i.
+inline int64_t i8kv_key_tiles(int Nq, int Nk, int pos0) {
+  const int64_t last = std::min<int64_t>(Nk, (int64_t)pos0 + Nq);
+  return (last + kBlk - 1) / kBlk;
+}
+
 }  // namespace
 
 extern "C" {
@@ -60,6 +76,7 @@ const char* qattn_status_string(int status) {
     case QATTN_EUNSUPPORTED: return "unsupported head dimension (D must be 64 or 128)";
     case QATTN_EWORKSPACE: return "workspace too small";
     case QATTN_EHIP: return "HIP kernel launch failed";
+    case QATTN_ESCRATCH: return "the call needs a larger workspace than the library's static scratch array holds";
     default: return "unknown status";
   }
 }
@@ -127,16 +144,6 @@ int qattn_prep(const void* q, const int64_t q_str[3], const void* k, const int64
   return status_of(launch_prep(p, D, (hipStream_t)stream));
 }
 
-static bool out_ok(const void* out, const int64_t* str, int n, int out_dtype) {
-  if (!out || !str) return false;
-  if (out_dtype != QATTN_OUT_BF16 && out_dtype != QATTN_OUT_F32) return false;
-  const int esz = out_dtype == QATTN_OUT_BF16 ? 2 : 4;
-  if (!aligned(out, 4 * esz)) return false;
-  for (int i = 0; i < n; ++i)
-    if (str[i] < 0 || (str[i] & 3) != 0) return false;
-  return true;
-}
-
 int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const float* k_scale, const uint16_t* vbf,
               const float* v_scale, int B, int H, int Nq, int Nk, int D, float scale_log2, int causal, void* out,
               const int64_t out_str[3], int out_dtype, void* stream) {
@@ -183,12 +190,6 @@ int qattn_fwd(const int8_t* q8, const float* q_scale, const int8_t* k8, const fl
   return status_of(launch_attn_fwd(a, D, (hipStream_t)stream));
 }
 
-// Key tiles a causal prefill reads: every query sees keys 0 .. pos0 + i.
-static int64_t i8kv_key_tiles(int Nq, int Nk, int pos0) {
-  const int64_t last = std::min<int64_t>(Nk, (int64_t)pos0 + Nq);
-  return (last + kBlk - 1) / kBlk;
-}
-
 int qattn_fwd_i8kv_kv_splits(int H, int Nq, int Nk, int pos0) {
   if (H <= 0 || Nq <= 0 || Nk <= 0 || pos0 < 0 || (int64_t)pos0 + Nq > Nk) return 0;
   const int64_t wgs = (int64_t)H * ((Nq + 255) / 256);  // workgroups of one pass
@@ -215,22 +216,71 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
                    const int8_t* v_cache, const float* v_tok_scale, int H, int Nq, int Nk, int D, int pos0,
                    float scale_log2, int kv_splits, void* workspace, size_t workspace_bytes, void* out,
                    const int64_t out_str[2], int out_dtype, void* stream) {
-  if (!k_cache || !k_tok_scale || !v_cache || !v_tok_scale || !workspace) return QATTN_EINVAL;
+  if (!workspace) return QATTN_EINVAL;
+  size_t need = 0;
+  const int st = qattn::i8kv_check(q, q_str, k_cache, k_tok_scale, v_cache, v_tok_scale, H, Nq, Nk, D, pos0,
+                                   scale_log2, &kv_splits, out, out_str, out_dtype, &need);
+  if (st != QATTN_OK) return st;
+  if (!aligned(workspace, 256)) return QATTN_EINVAL;
+  if (workspace_bytes < need) return QATTN_EWORKSPACE;
+  return qattn::i8kv_launch(q, q_str, k_cache, k_tok_scale, v_cache, v_tok_scale, H, Nq, Nk, D, pos0, scale_log2,
+                            kv_splits, workspace, out, out_str, out_dtype, stream);
+}
+
+int qattn_kv_append_i8(const void* x, const int64_t x_str[2], int Nnew, int H, int D, int8_t* cache,
+                       float* tok_scale, int Nmax, int pos, void* stream) {
+  if (!cache || !tok_scale) return QATTN_EINVAL;
+  if (!bf16_view_ok(x, x_str, 2)) return QATTN_EINVAL;
+  if (!sizes_ok(1, H, Nnew) || Nmax <= 0 || Nmax > kMaxN) return QATTN_EINVAL;
+  if (D != 64 && D != 128) return QATTN_EUNSUPPORTED;
+  if (pos < 0 || (int64_t)pos + Nnew > Nmax) return QATTN_EINVAL;
+  if ((int64_t)H * Nmax * D > ((int64_t)1 << 40)) return QATTN_EINVAL;
+  if (!aligned(cache, 8) || !aligned(tok_scale, 4)) return QATTN_EINVAL;
+  return status_of(launch_kv_append_i8(x, x_str[0], x_str[1], Nnew, H, D, cache, tok_scale, Nmax, pos,
+                                       (hipStream_t)stream));
+}
+
+int qattn_selftest_p8_codes(const float* u, uint8_t* codes, int64_t n, int saturating, void* stream) {
+  if (!u || !codes || n <= 0 || (saturating != 0 && saturating != 1)) return QATTN_EINVAL;
+  if (!aligned(u, 4)) return QATTN_EINVAL;
+  return status_of(launch_p8_codes(u, codes, n, saturating, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace qattn {
+
+// Validation of a prefill call, everything but the workspace: resolves *kv_splits (0 =
+// the rule) and returns the workspace size in *need.
+int i8kv_check(const void* q, const int64_t q_str[2], const int8_t* k_cache, const float* k_tok_scale,
+               const int8_t* v_cache, const float* v_tok_scale, int H, int Nq, int Nk, int D, int pos0,
+               float scale_log2, int* kv_splits, const void* out, const int64_t out_str[2], int out_dtype,
+               size_t* need) {
+  if (!k_cache || !k_tok_scale || !v_cache || !v_tok_scale || !kv_splits || !need) return QATTN_EINVAL;
   if (!bf16_view_ok(q, q_str, 2)) return QATTN_EINVAL;
   if (!sizes_ok(1, H, Nq) || !sizes_ok(1, H, Nk)) return QATTN_EINVAL;
   if (D != 64 && D != 128) return QATTN_EUNSUPPORTED;
   if (pos0 < 0 || (int64_t)pos0 + Nq > Nk || !slice_ok(Nk, D)) return QATTN_EINVAL;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_tok_scale, 4) || !aligned(v_tok_scale, 4))
     return QATTN_EINVAL;
-  if (!aligned(workspace, 256)) return QATTN_EINVAL;
   if (!out_ok(out, out_str, 2, out_dtype)) return QATTN_EINVAL;
   if (isnan(scale_log2) || isinf(scale_log2)) return QATTN_EINVAL;
-  if (kv_splits == 0) kv_splits = qattn_fwd_i8kv_kv_splits(H, Nq, Nk, pos0);
-  if (kv_splits < 1 || kv_splits > kMaxKvSplits) return QATTN_EINVAL;
-  if ((int64_t)H * ((Nq + 255) / 256) * kv_splits > INT32_MAX) return QATTN_EINVAL;
-  const size_t need = qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, kv_splits);
-  if (need == 0) return QATTN_EINVAL;
-  if (workspace_bytes < need) return QATTN_EWORKSPACE;
+  int S = *kv_splits;
+  if (S == 0) S = qattn_fwd_i8kv_kv_splits(H, Nq, Nk, pos0);
+  if (S < 1 || S > kMaxKvSplits) return QATTN_EINVAL;
+  if ((int64_t)H * ((Nq + 255) / 256) * S > INT32_MAX) return QATTN_EINVAL;
+  *need = qattn_fwd_i8kv_workspace_bytes(H, Nq, Nk, D, S);
+  if (*need == 0) return QATTN_EINVAL;
+  *kv_splits = S;
+  return QATTN_OK;
+}
+
+// The launches of a validated prefill call into a workspace of at least the checked size
+// (256-byte aligned): the preparation of q and of the cached V, then the fused loop.
+int i8kv_launch(const void* q, const int64_t q_str[2], const int8_t* k_cache, const float* k_tok_scale,
+                const int8_t* v_cache, const float* v_tok_scale, int H, int Nq, int Nk, int D, int pos0,
+                float scale_log2, int kv_splits, void* workspace, void* out, const int64_t out_str[2],
+                int out_dtype, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int64_t nkp = npad64(Nk), nqp = npad64(Nq);
   uint8_t* ws = (uint8_t*)workspace;
@@ -303,23 +353,5 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
   return status_of(launch_attn_fwd(a, D, st));
 }
 
-int qattn_kv_append_i8(const void* x, const int64_t x_str[2], int Nnew, int H, int D, int8_t* cache,
-                       float* tok_scale, int Nmax, int pos, void* stream) {
-  if (!cache || !tok_scale) return QATTN_EINVAL;
-  if (!bf16_view_ok(x, x_str, 2)) return QATTN_EINVAL;
-  if (!sizes_ok(1, H, Nnew) || Nmax <= 0 || Nmax > kMaxN) return QATTN_EINVAL;
-  if (D != 64 && D != 128) return QATTN_EUNSUPPORTED;
-  if (pos < 0 || (int64_t)pos + Nnew > Nmax) return QATTN_EINVAL;
-  if ((int64_t)H * Nmax * D > ((int64_t)1 << 40)) return QATTN_EINVAL;
-  if (!aligned(cache, 8) || !aligned(tok_scale, 4)) return QATTN_EINVAL;
-  return status_of(launch_kv_append_i8(x, x_str[0], x_str[1], Nnew, H, D, cache, tok_scale, Nmax, pos,
-                                       (hipStream_t)stream));
-}
 
-int qattn_selftest_p8_codes(const float* u, uint8_t* codes, int64_t n, int saturating, void* stream) {
-  if (!u || !codes || n <= 0 || (saturating != 0 && saturating != 1)) return QATTN_EINVAL;
-  if (!aligned(u, 4)) return QATTN_EINVAL;
-  return status_of(launch_p8_codes(u, codes, n, saturating, (hipStream_t)stream));
-}
-
-}  // extern "C"
+}  // namespace qattn

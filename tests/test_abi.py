@@ -38,6 +38,7 @@ def lib():
     L.qattn_fwd_i8kv_kv_splits.restype = I
     L.qattn_selftest_p8_codes.argtypes = [P, P, ct.c_int64, ct.c_int, P]
     L.qattn_kv_append_i8.argtypes = [P, I64x2, I, I, I, P, P, I, I, P]
+    L.qattn_fwd_i8kv_noalloc.argtypes = [P, I64x2, P, P, P, P, I, I, I, I, I, F, I, P, I64x2, I, P]
     L.qattn_status_string.argtypes = [I]
     L.qattn_status_string.restype = ct.c_char_p
     return L
@@ -62,7 +63,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert lib.qattn_status_string(s)
     assert b"unknown" in lib.qattn_status_string(7)
 
@@ -220,3 +221,18 @@ def test_product_path_does_not_use_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text and "qattn_oracle" not in text, f
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free prefill call checks its arguments like qattn_fwd_i8kv and
+    refuses a call whose workspace exceeds its static array, all before any HIP call."""
+    st = I64x2(32 * 128, 128)
+
+    def call(H=32, Nq=1024, Nk=65536, D=128, pos0=64512, q=A, k=A, out=A):
+        return lib.qattn_fwd_i8kv_noalloc(q, st, k, A, A, A, H, Nq, Nk, D, pos0, 0.0, 0, out, st, 1, None)
+
+    assert call() == -5  # 32 heads over 64K cached tokens: beyond the static workspace
+    assert call(q=None) == EINVAL
+    assert call(pos0=65000) == EINVAL  # pos0 + Nq > Nk
+    assert call(D=96) == EUNSUP
+    assert call(out=A + 4) == EINVAL
