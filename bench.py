@@ -36,17 +36,25 @@ PEAK_HBM_GBPS = 8000.0
 DEFAULT_WORKLOAD = W.VIDEO37810.name
 KERNEL_SRC = os.path.join(ROOT, "quantized_attention_qattn_amd", "csrc", "attn_fwd.hip")
 
-# HBM traffic of the fused kernel per launch, from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE passes over this script (KiB per dispatch), scaled by what the same counters
-# read for a copy of known size (--calibrate-copy).  Keyed by the SHA-256 of the kernel
-# source the counters were taken on: any other source reports traffic as null.
-MEASURED_TRAFFIC = {
-    "7dfcd30d00eef8807e8f2dbda54e27605cd7822d138be3904e6583bf7fc84055": {
+# Counters of the fused kernel per launch, from rocprofv3 --pmc passes over this script:
+# HBM traffic from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by what the same
+# counters read for a copy of known size (--calibrate-copy), and SQ_INSTS_VALU (wave-level
+# VALU instructions per dispatch).  Keyed by the SHA-256 of the kernel source the counters
+# were taken on: any other source reports them as null.
+MEASURED_COUNTERS = {
+    "993dfbd5b29302dcea70aa0448fd86e61b65b9ddb91855a8689303e386a51830": {
         "workload": "video_dit_b1_h24_n37810_d128",
-        "fetch_kib": 965057.3, "fetch_scale": 1048576.0 / 524309.0,  # 1 GiB copy read as 524309 KiB
-        "write_kib": 230823.5, "write_scale": 1048576.0 / 1048576.0,
+        "fetch_kib": 964988.4, "fetch_scale": 1048576.0 / 524309.0,  # 1 GiB copy read as 524309 KiB
+        "write_kib": 231091.4, "write_scale": 1048576.0 / 1048576.0,
+        "valu_insts": 3.85629e+09,
     },
 }
+# VALU budget per score element at the MFMA peak: a CU retires 8,192 INT8/FP8 MFMA ops per
+# clock and a score costs 4 D of them (QK and PV), i.e. 16 scores per clock at D = 128,
+# against 64 fp32 VALU lanes per clock: 4 lane-ops per score.  With P.V on the bf16 MFMA
+# (4,096 ops per clock) a score costs 2 D / 8192 + 2 D / 4096 clocks: 6 lane-ops.
+VALU_LANES_PER_CU_CLK = 64
+MFMA_OPS_PER_CU_CLK = {"int8_fp8": 8192, "bf16": 4096}
 
 
 def parse():
@@ -394,9 +402,11 @@ def run(args, sampler):
                  "cold_gbps": round(prep_bytes / (pc["p50"] * 1e-3) / 1e9, 1)}
 
     sha = kernel_sha()
-    tr = MEASURED_TRAFFIC.get(sha)
+    tr = MEASURED_COUNTERS.get(sha)
+    if tr is not None and tr["workload"] != w.name:
+        tr = None
     traffic = None
-    if tr is not None and tr["workload"] == w.name:
+    if tr is not None:
         traffic = round((tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]) * 1024.0)
     roof = {"bound": "mfma", "kernel": kernel_name, "achieved": round(achieved, 3), "peak": PEAK_INT8_FP8_TOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_FP8_TOPS, 4), "traffic": traffic,
@@ -405,11 +415,25 @@ def run(args, sampler):
             "sclk_samples": 0 if not clocks else len(clocks),
             "frac_at_measured_sclk": None if sclk is None else
             round(achieved / (PEAK_INT8_FP8_TOPS * sclk / NOMINAL_SCLK_MHZ), 4)}
-    if qa.PV_INSTRUCTION.endswith("bf16"):
+    pv_bf16 = qa.PV_INSTRUCTION.endswith("bf16")
+    if pv_bf16:
         # the instructions actually issued: half the ops on INT8 MFMA (5.0 POPS), half on bf16 MFMA (2.5)
         mix = 1.0 / (0.5 / PEAK_INT8_FP8_TOPS + 0.5 / PEAK_BF16_TOPS)
         roof["peak_of_issued_mix"] = round(mix, 1)
         roof["frac_of_issued_mix"] = round(achieved / mix, 4)
+    # secondary roofline: VALU lane-operations per score element (SQ_INSTS_VALU x 64 lanes
+    # over the scores the metric counts) against the per-score VALU budget at the MFMA peak
+    valu = None
+    if tr is not None and "valu_insts" in tr:
+        scores = ops / (4.0 * w.D)
+        per_score = tr["valu_insts"] * 64 / scores
+        clk_int8 = 4.0 * w.D / MFMA_OPS_PER_CU_CLK["int8_fp8"]
+        clk_mix = 2.0 * w.D / MFMA_OPS_PER_CU_CLK["int8_fp8"] + 2.0 * w.D / MFMA_OPS_PER_CU_CLK["bf16"]
+        valu = {"counter": "SQ_INSTS_VALU", "lane_ops_per_score": round(per_score, 3),
+                "budget_at_int8_fp8_peak": round(VALU_LANES_PER_CU_CLK * clk_int8, 3),
+                "budget_at_issued_mix": round(VALU_LANES_PER_CU_CLK * (clk_mix if pv_bf16 else clk_int8), 3),
+                "frac_of_peak_allowed_at_full_valu_rate": round(min(1.0, VALU_LANES_PER_CU_CLK * clk_int8 / per_score), 4)}
+    roof["valu"] = valu
     rec = {
         "metric": "attention TOPS (4*N_q*N_k*D*H / step time) on one MI355X",
         "value": round(value, 3),

@@ -167,6 +167,11 @@ def test_fwd_validation(lib):
     assert call(st=I64x3(1024, 130, 64)) == EINVAL
     assert call(sl=float("nan")) == EINVAL
     assert call(H=0) == EINVAL
+    assert call(Nq=0) == EINVAL  # empty inputs are refused, not launched
+    assert call(Nk=0) == EINVAL
+    assert call(Nk=(1 << 28) + 1) == EINVAL  # beyond the largest token count
+    assert call(Nk=1 << 24, D=128) == EINVAL  # a (b, h) slice of 2^31 code bytes: past 32-bit offsets
+    assert call(Nk=1 << 25, D=64) == EINVAL
 
 
 def test_i8kv_validation(lib):
