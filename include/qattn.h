@@ -144,7 +144,8 @@ int qattn_fwd_i8kv(const void* q, const int64_t q_str[2], const int8_t* k_cache,
  * QATTN_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on (kept until the process ends).
  * The call allocates nothing.  Returns QATTN_ESCRATCH, before any launch, when the call
  * would need a larger workspace than that (qattn_fwd_i8kv_workspace_bytes with the
- * resolved kv_splits), e.g. 32 heads of D = 128 and 512 queries over 24K or more cached tokens;
+ * resolved kv_splits), e.g. 32 heads of D = 128 and 512 or 1,024 queries over 28K or
+ * more cached tokens;
  * every other argument is checked as by qattn_fwd_i8kv.  All calls on one GPU share its
  * array: calls that overlap on one GPU (other streams, other threads) race and give
  * undefined results.  A call leaves its intermediates in the array; nothing needs to be
@@ -165,7 +166,7 @@ int qattn_fwd_i8kv_noalloc(const void* q, const int64_t q_str[2], const int8_t* 
 size_t qattn_fwd_i8kv_workspace_bytes(int H, int Nq, int Nk, int D, int kv_splits);
 
 /* The key-range count qattn_fwd_i8kv uses for kv_splits = 0 (host only, no GPU call):
- * ceil(512 / (H * ceil(Nq / 256))) -- about two workgroups per CU -- capped so that every
+ * ceil(256 / (H * ceil(Nq / 256))) -- one workgroup per CU -- capped so that every
  * range holds at least 16 key tiles and at 64, at least 1.  Returns 0 for invalid sizes
  * (0 <= pos0, pos0 + Nq <= Nk). */
 int qattn_fwd_i8kv_kv_splits(int H, int Nq, int Nk, int pos0);

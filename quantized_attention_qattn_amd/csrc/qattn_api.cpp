@@ -15,9 +15,9 @@ namespace {
 
 constexpr int64_t kMaxN = (int64_t)1 << 28;  // keeps every row index and grid size in range
 constexpr int kMaxGridYZ = 65535;
-// Split-KV rule for the prefill entry point: enough key ranges for about two waves of
-// workgroups over the 256 CUs, each range at least kSplitMinTiles key tiles long.
-constexpr int64_t kSplitTargetWorkgroups = 512;
+// Split-KV rule for the prefill entry point: enough key ranges for one workgroup per CU
+// (256 CUs, one resident workgroup each), each range at least kSplitMinTiles key tiles long.
+constexpr int64_t kSplitTargetWorkgroups = 256;
 constexpr int64_t kSplitMinTiles = 16;
 constexpr int kMaxKvSplits = 64;
 

@@ -83,9 +83,9 @@ def test_workspace_bytes(lib):
 
 
 def test_kv_split_rule(lib):
-    # ceil(512 / (H * ceil(Nq / 256))), at least 16 key tiles per range, at most 64, at least 1
-    assert lib.qattn_fwd_i8kv_kv_splits(32, 1024, 32768, 31744) == 4  # 128 workgroups, 512 tiles
-    assert lib.qattn_fwd_i8kv_kv_splits(32, 512, 65536, 65024) == 8  # 64 workgroups, 1024 tiles
+    # ceil(256 / (H * ceil(Nq / 256))), at least 16 key tiles per range, at most 64, at least 1
+    assert lib.qattn_fwd_i8kv_kv_splits(32, 1024, 32768, 31744) == 2  # 128 workgroups, 512 tiles
+    assert lib.qattn_fwd_i8kv_kv_splits(32, 512, 65536, 65024) == 4  # 64 workgroups, 1024 tiles
     assert lib.qattn_fwd_i8kv_kv_splits(2, 64, 128, 64) == 1  # 2 tiles: no split
     assert lib.qattn_fwd_i8kv_kv_splits(1, 1, 65536, 100) == 1  # 2 visible tiles
     assert lib.qattn_fwd_i8kv_kv_splits(1, 1, 65536, 65535) == 64  # one query, 1024 tiles: capped at 64

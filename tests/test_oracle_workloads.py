@@ -80,11 +80,11 @@ def _i8kv_readings(orc, w, heads):
 
 def _kv_splits(H, Nq, Nk, pos0):
     """The key-range count the library's rule gives for the whole workload (the prefill
-    result depends on it, so the oracle runs at the same count): about two workgroups of
-    256 query rows per CU over 256 CUs, ranges of at least 16 key tiles, at most 64."""
+    result depends on it, so the oracle runs at the same count): one workgroup of 256
+    query rows per CU over 256 CUs, ranges of at least 16 key tiles, at most 64."""
     wgs = H * ((Nq + 255) // 256)
     T = (min(Nk, pos0 + Nq) + TILE - 1) // TILE
-    return max(1, min((512 + wgs - 1) // wgs, T // 16, 64))
+    return max(1, min((256 + wgs - 1) // wgs, T // 16, 64))
 
 
 CASES = [
