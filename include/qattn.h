@@ -23,8 +23,10 @@
  *   - N_pad = ceil(N / 64) * 64.  Code layouts are zero-padded to N_pad rows/columns.
  *   - Results are bitwise deterministic run to run (no atomics).
  *   - NaN/Inf inputs are outside the contract (their codes are unspecified).
- *   - Calls on different streams that share output buffers race; the library holds no
- *     global mutable state, so calls are otherwise thread-safe.
+ *   - Calls on different streams that share output buffers race.  Apart from the
+ *     scratch array of qattn_fwd_i8kv_noalloc (shared by that call on each GPU; see
+ *     there), the library holds no global mutable state, so calls are otherwise
+ *     thread-safe.
  */
 #ifndef QATTN_H
 #define QATTN_H
